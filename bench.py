@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the fused dense-and-sparse LUT GEMV y = (D + S) x on one MI355X.
+
+One step = one pass over the whole weight stream of an 80-layer
+LLaMA-65B-shaped model at batch 1: 80 x (q, k, v, o 8192x8192; gate, up
+22016x8192; down 8192x22016) = 560 calls of sqllm_dense_sparse_gemv, 3-bit
+codes with per-row 8-entry fp16 tables and 0.45% fp16 CSR outliers, each with
+its own fp16 activation vector, back to back on one stream.  Inputs are seeded
+synthetic data of those shapes and distributions (no trained weights), all
+resident in HBM before the timed region (24.3 GB of codes + 1.2 GB of CSR).
+
+Metric: effective HBM GB/s = algorithmic bytes per step (codes at exactly b
+bits + fp16 tables + CSR at 4 B per nonzero + int32 row pointers + x + y)
+divided by the time per step; also microseconds per GEMV.  The pages' kernel
+ran on other hardware and prints no GB/s figure, so vs_baseline is null.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU (sharding by output rows is described in the design notes).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--bits", type=int, default=3, choices=(3, 4))
+    p.add_argument("--density-bp", type=int, default=45, help="outlier density in basis points (45 = 0.45%%)")
+    p.add_argument("--layers", type=int, default=80)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-graph", action="store_true", help="time plain launches only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
+    return p.parse_args()
+
+
+class WeightStream:
+    """Device-resident weight stream; launches go through the C ABI with
+    arguments marshalled once."""
+
+    def __init__(self, specs, seed: int, workload_id: int = 5, progress_every: int = 70):
+        import numpy as np
+        import torch
+
+        import non_uniform_weight_amd as nw
+        import synth
+
+        self.nw, self.torch, self.np = nw, torch, np
+        self.specs = specs
+        self.bits = specs[0].bits
+        self.mats = []
+        self.bytes_per_step = 0
+        rows_max = max(s.rows for s in specs)
+        cols_max = max(s.cols for s in specs)
+        batch = max(s.batch for s in specs)
+        self.ws = torch.zeros(max(nw.workspace_bytes(rows_max, cols_max, batch), 256), dtype=torch.uint8,
+                              device="cuda")
+        t0 = time.time()
+        for i, spec in enumerate(specs):
+            m = synth.make_matrix(spec, seed=seed, workload=workload_id, index=i)
+            codes = torch.from_numpy(m.codes).cuda()
+            packed = nw.pack(codes, spec.bits)
+            del codes
+            d = {
+                "spec": spec,
+                "packed": packed,
+                "lut": torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16),
+                "row_ptr": torch.from_numpy(m.row_ptr).cuda(),
+                "col": torch.from_numpy(m.col.view(np.int16)).cuda() if m.col.size else None,
+                "val": torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16) if m.col.size else None,
+                "x": torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16),
+                "y": torch.empty((spec.batch, spec.rows), dtype=torch.float16, device="cuda"),
+                "nnz": int(m.col.size),
+            }
+            d["bytes"] = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, d["nnz"], spec.batch)
+            self.bytes_per_step += d["bytes"]
+            self.mats.append(d)
+            if (i + 1) % progress_every == 0 or i + 1 == len(specs):
+                log(f"resident: {i + 1}/{len(specs)} matrices, {self.bytes_per_step / 1e9:.2f} GB, "
+                    f"{time.time() - t0:.0f} s")
+        torch.cuda.synchronize()
+        self._marshal()
+
+    def _marshal(self):
+        lib = self.nw.library()
+        self.fn = lib.sqllm_dense_sparse_gemv
+        vp = ctypes.c_void_p
+        self.calls = []
+        for d in self.mats:
+            s = d["spec"]
+            nnz = d["nnz"]
+            self.calls.append((
+                vp(d["packed"].data_ptr()), vp(d["lut"].data_ptr()), s.bits,
+                vp(d["row_ptr"].data_ptr()) if nnz else None,
+                vp(d["col"].data_ptr()) if nnz else None,
+                vp(d["val"].data_ptr()) if nnz else None,
+                nnz, s.rows, s.cols, vp(d["x"].data_ptr()), s.batch, vp(d["y"].data_ptr()),
+                vp(self.ws.data_ptr()), self.ws.numel()))
+
+    def step(self, stream) -> None:
+        fn, h = self.fn, vp_stream(stream)
+        for args in self.calls:
+            st = fn(*args, h)
+            if st != 0:
+                raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
+
+    def launch_durations_ms(self, stream):
+        """Per-launch kernel time from HIP events recorded on the launch stream."""
+        torch = self.torch
+        fn, h = self.fn, vp_stream(stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in self.calls]
+        with torch.cuda.stream(stream):
+            for (e0, e1), args in zip(ev, self.calls):
+                e0.record(stream)
+                fn(*args, h)
+                e1.record(stream)
+        stream.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def vp_stream(stream):
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def cpu_baseline(stream_specs, seed: int, threads: int):
+    """The oracle as it stands, on layer 0 (7 linears, every row)."""
+    import oracle
+    import synth
+
+    import non_uniform_weight_amd as nw
+
+    sample = stream_specs[:7]
+    total_bytes = 0
+    elapsed = 0.0
+    for i, spec in enumerate(sample):
+        m = synth.make_matrix(spec, seed=seed, workload=5, index=i)
+        t0 = time.perf_counter()
+        oracle.dense_sparse_gemv(m.codes, m.lut, spec.bits, m.row_ptr if m.col.size else None, m.col, m.val, m.x,
+                                 threads=threads)
+        elapsed += time.perf_counter() - t0
+        total_bytes += nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, int(m.col.size), spec.batch)
+    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of the stream: 7 linears, all rows ({total_bytes / 1e6:.1f} MB algorithmic), "
+                      f"fp64 oracle incl. the |W||x| normaliser, {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the design notes describe row sharding across GPUs).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    specs = synth.workload(5, bits=args.bits, density_bp=args.density_bp)[:7 * args.layers]
+    ws = WeightStream(specs, args.seed)
+    n_calls = len(ws.calls)
+    stream = torch.cuda.Stream()
+
+    # plain launches
+    for _ in range(args.warmup):
+        ws.step(stream)
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        ws.step(stream)
+    e1.record(stream)
+    stream.synchronize()
+    ms_direct = e0.elapsed_time(e1) / args.steps
+    log(f"plain launches: {ms_direct:.3f} ms/step")
+
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            ws.step(stream)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            for _ in range(args.warmup):
+                g.replay()
+            stream.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        ms_graph = e0.elapsed_time(e1) / args.steps
+        log(f"graph replay: {ms_graph:.3f} ms/step")
+
+    durs = ws.launch_durations_ms(stream)
+    avg_launch_ms = sum(durs) / len(durs)
+    avg_bytes = ws.bytes_per_step / n_calls
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    log(f"per-launch (events): {avg_launch_ms * 1e3:.2f} us avg, {achieved:.0f} GB/s")
+
+    ms = min(ms_direct, ms_graph) if ms_graph is not None else ms_direct
+    value = ws.bytes_per_step / (ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(specs, args.seed, threads)
+        log(f"cpu baseline: {cpu['value']} GB/s with {threads} threads")
+
+    out = {
+        "metric": "effective HBM GB/s (% of peak) and us/GEMV, 3-bit LUT+sparse, batch 1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"u{args.bits}-lut-f16/f32-acc",
+        "data": "synthetic",
+        "config": {
+            "workload": f"80-layer LLaMA-65B-shaped weight stream, {n_calls} GEMVs "
+                        f"(8192x8192 x4, 22016x8192 x2, 8192x22016 per layer), {args.bits}-bit codes, "
+                        f"{args.density_bp / 100:.2f}% uniform CSR outliers, batch 1",
+            "bits": args.bits,
+            "outlier_density_pct": args.density_bp / 100,
+            "batch": 1,
+            "gemvs_per_step": n_calls,
+            "bytes_per_step": ws.bytes_per_step,
+            "launch": "HIP graph replay" if ms_graph is not None and ms_graph <= ms_direct else "plain launches",
+        },
+        "us_per_gemv": round(ms * 1e3 / n_calls, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_plain": round(ms_direct, 4),
+        "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"dense_sparse_kernel<{args.bits},1,dense,sparse>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": round(avg_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

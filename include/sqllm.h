@@ -1,0 +1,181 @@
+/*
+ * sqllm.h -- C ABI of the dense-and-sparse LUT matrix-vector product
+ * y = (D + S) x on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (SqueezeLLM: Dense-and-Sparse Quantization, summary page):
+ *   - §3.4 "The Dense-and-Sparse Decomposition": W = D + S.  S holds the few
+ *     outlier / sensitive weights in CSR form with fp16 values, 16-bit column
+ *     indices and row pointers (nnz of row i = row_ptr[i+1] - row_ptr[i]).
+ *   - §3.4 "Kernel Implementation": D is stored as a 2-D array of b-bit
+ *     indices (b = 3 or 4); index code[r][c] selects one of 2^b fp16
+ *     centroids in the lookup table of output channel r; the dequantized
+ *     weights multiply an fp16 activation vector.  A balanced sparse kernel
+ *     computes S x, fused with the dense part into one output.
+ *   - §3.4 "The 3/4-bit storage format": every index takes exactly b bits.
+ *   - §3.4 "The Memory-Bound Analysis": batch-1 generation is a
+ *     matrix-vector product; batches up to 8 are accepted here.
+ *
+ *   y[b][r] = sum_c LUT[r][code[r][c]] * x[b][c]
+ *           + sum_{i=row_ptr[r]}^{row_ptr[r+1]-1} val[i] * x[b][col_idx[i]]
+ *
+ * Arithmetic: every product of two fp16 values is formed exactly and summed
+ * in fp32; the fused call rounds each output once to fp16 (round to nearest
+ * even).  Summation order is fixed, so repeated calls give identical bits.
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees memory on the hot calls and keeps no state
+ *     between calls (the workspace below is the caller's).
+ *   - fp16 values are passed as raw IEEE binary16 bit patterns (uint16_t).
+ *   - Layouts are row-major and contiguous:
+ *       lut  [rows][2^bits]          16-byte aligned
+ *       x    [batch][cols]           4-byte aligned
+ *       y    [batch][rows]           4-byte aligned
+ *       row_ptr [rows+1] int32, col_idx [nnz] uint16, val [nnz] fp16
+ *     i.e. y = x W^T with W = [rows][cols] = out x in features.
+ *   - Hot calls are asynchronous on `stream` (NULL = default stream), never
+ *     synchronise, and report only argument errors (checked on the host
+ *     before any HIP call) and launch errors.
+ *   - Preconditions not checked on the hot path (violations are undefined
+ *     behaviour): row_ptr[0] == 0, row_ptr[rows] == nnz, row_ptr
+ *     non-decreasing, col_idx[i] < cols, x and y do not overlap, inputs finite.
+ *     Duplicate (row, column) outlier entries are summed.
+ *   - rows >= 1; cols >= 256 and a multiple of 256; cols <= 65536 when
+ *     outliers are given (16-bit column indices); nnz < 2^31; 1 <= batch <= 8.
+ *
+ * Packed code layout (the pages fix only "exactly b bits per index"; the
+ * arrangement below is this library's, chosen so that each 64-lane wave
+ * streams 1 KiB of codes per 128-bit load instruction):
+ *   rows are grouped in tiles of 64 (tile t = r / 64, lane l = r % 64), the
+ *   columns of a row in groups of 256 (g = c / 256, j = c % 256).  The 32*b
+ *   bytes that hold the 256 codes of (r, g) form one little-endian bit
+ *   string in which code j occupies bits [b*j, b*j + b).  That string is cut
+ *   into 2*b pieces of 16 bytes; piece q of (r, g) is stored at byte offset
+ *       ((t * G + g) * 2b + q) * 1024 + l * 16,      G = cols / 256.
+ *   Rows of the last tile beyond `rows` are padding (zero after sqllm_pack).
+ *   Total size: sqllm_packed_bytes() = ceil(rows / 64) * 64 * cols * b / 8.
+ *   The packed buffer must be 16-byte aligned.
+ *
+ * Workspace: the hot calls split long rows across workgroups and combine
+ * the fp32 partial sums on the device.  They take a caller-owned workspace
+ * of at least sqllm_workspace_bytes(rows, cols, batch) bytes (a multiple of
+ * 4), 256-byte aligned, ZERO-FILLED before its first use.  Partial sums are
+ * kept from its start and one arrival counter per 64-row tile in its last
+ * 4 * ceil(rows / 64) bytes.  Every call leaves it ready for the next one
+ * (its counters return to zero when the call's kernel ends), so one
+ * workspace can serve any sequence of calls, of any shapes it is large
+ * enough for, that are ordered on one stream.  Calls that may run
+ * concurrently need separate workspaces.
+ */
+#ifndef SQLLM_H
+#define SQLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQLLM_OK = 0,
+    SQLLM_ERR_NULL = 1,       /* a required pointer is NULL */
+    SQLLM_ERR_BITS = 2,       /* bits not 3 or 4 */
+    SQLLM_ERR_SHAPE = 3,      /* rows / cols / nnz out of range */
+    SQLLM_ERR_BATCH = 4,      /* batch not in [1, 8] */
+    SQLLM_ERR_ALIGN = 5,      /* a pointer is not aligned as required */
+    SQLLM_ERR_CODE_RANGE = 6, /* sqllm_pack: a code is >= 2^bits */
+    SQLLM_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed */
+    SQLLM_ERR_WORKSPACE = 8   /* workspace missing, misaligned or too small */
+} sqllm_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sqllm_status_string(sqllm_status s);
+
+/* Bytes of the packed code buffer for a rows x cols matrix of `bits`-bit
+ * codes (see the layout above); 0 if the arguments are out of range. */
+size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits);
+
+/* Bytes of workspace the hot calls need for this shape and batch (the same
+ * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv);
+ * 0 if the arguments are out of range. */
+size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch);
+
+/*
+ * sqllm_pack -- offline step: unpacked codes -> packed layout.
+ * Stores the b-bit indices with exactly b bits each (§3.4 "The 3/4-bit
+ * storage format").
+ *   codes:  device uint8 [rows][cols], every value < 2^bits
+ *   packed: device buffer of sqllm_packed_bytes(rows, cols, bits) bytes,
+ *           16-byte aligned; padding rows are written as zeros
+ * The code range is checked on the device; the call SYNCHRONISES `stream`
+ * to report SQLLM_ERR_CODE_RANGE (packed contents are then unspecified).
+ * It allocates (and frees) one 4-byte device flag.
+ */
+sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed,
+                        hipStream_t stream);
+
+/*
+ * sqllm_gemv -- dense part only: y = D x.
+ * §3.4 "Kernel Implementation", LUT-based dense kernel: stream the packed
+ * indices, look each one up in its row's fp16 table, multiply-add against
+ * the fp16 activations.
+ *   packed: sqllm_pack output; lut: fp16 [rows][2^bits]; x: fp16 [batch][cols]
+ *   y: fp16 [batch][rows], overwritten
+ */
+sqllm_status sqllm_gemv(const void *packed, const uint16_t *lut, int bits, int64_t rows, int64_t cols,
+                        const uint16_t *x, int batch, uint16_t *y, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * sqllm_spmv_add -- sparse part only: y += S x (read y, add, round once to
+ * fp16, write y).  §3.4 "Kernel Implementation", balanced sparse kernel:
+ * a fixed share of the nonzeros per thread, rows split across threads and
+ * their partial sums combined (here: in a fixed order).
+ *   nnz == 0 is a no-op; row_ptr / col_idx / val may then be NULL.
+ * With sqllm_gemv before it on the same stream this is the stream-ordered
+ * form of sqllm_dense_sparse_gemv (two fp16 roundings instead of one).
+ */
+sqllm_status sqllm_spmv_add(const int32_t *row_ptr, const uint16_t *col_idx, const uint16_t *val, int64_t nnz,
+                            int64_t rows, int64_t cols, const uint16_t *x, int batch, uint16_t *y,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sqllm_dense_sparse_gemv -- the fused product y = (D + S) x in one launch.
+ * §3.2 "Big-Picture Architecture" and §3.4 "Kernel Implementation" (kernel
+ * fusion): the dense and sparse contributions are summed on chip and each
+ * output is written once.  nnz == 0 gives exactly sqllm_gemv's result.
+ *   Arguments as for sqllm_gemv and sqllm_spmv_add; y is overwritten.
+ */
+sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, int bits, const int32_t *row_ptr,
+                                     const uint16_t *col_idx, const uint16_t *val, int64_t nnz, int64_t rows,
+                                     int64_t cols, const uint16_t *x, int batch, uint16_t *y, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Test-only exports (not part of the stable contract).  The readers are
+ * asynchronous on `stream`.
+ *   sqllm_test_unpack: packed -> uint8 codes [rows][cols]
+ *   sqllm_test_decode: packed + lut -> fp16 weights LUT[r][code[r][c]],
+ *                      [rows][cols] (exact bit copies of table entries)
+ */
+sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, int bits, uint8_t *codes,
+                               hipStream_t stream);
+/*   sqllm_test_tuning: set the launch configuration of later calls in this
+ *   process: waves per workgroup for 3-bit and 4-bit codes (1..8), the
+ *   workgroup count the column split aims for, and a forced split
+ *   (1..16).  0 restores a value's default (environment SQLLM_WAVES_3,
+ *   SQLLM_WAVES_4, SQLLM_TARGET_WGS, SQLLM_SPLIT, else built in).  Results
+ *   agree within the stated tolerance for every configuration; not
+ *   thread-safe against concurrent calls. */
+sqllm_status sqllm_test_tuning(int waves3, int waves4, int target_wgs, int split);
+sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
+                               uint16_t *w, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQLLM_H */

@@ -1,0 +1,215 @@
+"""MI355X (gfx950) dense-and-sparse LUT matrix-vector product y = (D + S) x.
+
+Thin ctypes binding over ``libsqllm.so`` (see ``include/sqllm.h``): it checks
+tensor dtypes, shapes and devices, passes raw device pointers and the current
+HIP stream, and turns status codes into exceptions.  Every step of the
+product runs in the library's HIP kernels; there is no fallback path.  If the
+library has not been built (``__graft_entry__.build()`` or
+``python non_uniform_weight_amd/_build.py``) importing this package raises.
+
+The operation follows SqueezeLLM: Dense-and-Sparse Quantization (summary
+page), §3.4 "The Dense-and-Sparse Decomposition" (W = D + S, S in CSR) and
+"Kernel Implementation" (LUT-based dense kernel, balanced sparse kernel,
+fused into one launch).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime first, so libsqllm.so binds to the same one
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsqllm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python non_uniform_weight_amd/_build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_lib.sqllm_status_string.restype = ctypes.c_char_p
+_lib.sqllm_status_string.argtypes = [_i32]
+_lib.sqllm_packed_bytes.restype = _sz
+_lib.sqllm_packed_bytes.argtypes = [_i64, _i64, _i32]
+_lib.sqllm_workspace_bytes.restype = _sz
+_lib.sqllm_workspace_bytes.argtypes = [_i64, _i64, _i32]
+_lib.sqllm_pack.restype = _i32
+_lib.sqllm_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+_lib.sqllm_gemv.restype = _i32
+_lib.sqllm_gemv.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]
+_lib.sqllm_spmv_add.restype = _i32
+_lib.sqllm_spmv_add.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]
+_lib.sqllm_dense_sparse_gemv.restype = _i32
+_lib.sqllm_dense_sparse_gemv.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                         _sz, _vp]
+_lib.sqllm_test_unpack.restype = _i32
+_lib.sqllm_test_unpack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+_lib.sqllm_test_tuning.restype = _i32
+_lib.sqllm_test_tuning.argtypes = [_i32, _i32, _i32, _i32]
+_lib.sqllm_test_decode.restype = _i32
+_lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
+
+EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes", "sqllm_pack", "sqllm_gemv",
+           "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_test_unpack", "sqllm_test_decode",
+           "sqllm_test_tuning")
+
+SQLLM_OK = 0
+
+
+class SqllmError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_lib.sqllm_status_string(status).decode()}")
+
+
+def _check(status: int, call: str) -> None:
+    if status != SQLLM_OK:
+        raise SqllmError(status, call)
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: torch.Tensor expected")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: device tensor expected (the product runs only on the GPU)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {dtype} expected, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous tensor expected")
+    return t.data_ptr()
+
+
+def packed_bytes(rows: int, cols: int, bits: int) -> int:
+    return int(_lib.sqllm_packed_bytes(rows, cols, bits))
+
+
+def workspace_bytes(rows: int, cols: int, batch: int) -> int:
+    return int(_lib.sqllm_workspace_bytes(rows, cols, batch))
+
+
+_WORKSPACES: dict = {}
+
+
+def workspace(rows: int, cols: int, batch: int, device=None) -> torch.Tensor:
+    """Zero-filled workspace cached per device (grown on demand).  Calls that
+    share it must be ordered on one stream."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    need = max(workspace_bytes(rows, cols, batch), 256)
+    ws = _WORKSPACES.get(device)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[device] = ws
+    return ws
+
+
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """uint8 codes [rows, cols] -> packed uint8 buffer (synchronises the stream)."""
+    rows, cols = codes.shape
+    n = packed_bytes(rows, cols, bits)
+    if n == 0:
+        raise ValueError(f"pack: unsupported shape/bits ({rows}, {cols}, {bits})")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    if out.numel() < n:
+        raise ValueError("pack: output buffer too small")
+    _check(_lib.sqllm_pack(_dev(codes, "codes", torch.uint8), rows, cols, bits, _dev(out, "packed", torch.uint8),
+                           _stream(stream)), "sqllm_pack")
+    return out
+
+
+def _x_y(x: torch.Tensor, y: torch.Tensor | None, rows: int):
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    batch, cols = x.shape
+    if y is None:
+        y = torch.empty((batch, rows), dtype=torch.float16, device=x.device)
+    if tuple(y.shape) != (batch, rows):
+        raise ValueError(f"y: shape {(batch, rows)} expected, got {tuple(y.shape)}")
+    return x, y, batch, cols
+
+
+def gemv(packed, lut, bits, x, y=None, ws=None, stream=None) -> torch.Tensor:
+    """y = D x (dense part)."""
+    rows = lut.shape[0]
+    x, y, batch, cols = _x_y(x, y, rows)
+    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    _check(_lib.sqllm_gemv(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16), bits, rows, cols,
+                           _dev(x, "x", torch.float16), batch, _dev(y, "y", torch.float16),
+                           _dev(ws, "workspace", torch.uint8), ws.numel(), _stream(stream)), "sqllm_gemv")
+    return y
+
+
+def _csr_ptrs(row_ptr, col, val):
+    nnz = int(col.numel()) if col is not None else 0
+    if nnz == 0:
+        return None, None, None, 0
+    col_dtype = torch.uint16 if col.dtype == torch.uint16 else torch.int16  # 16-bit column bits
+    return (_dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col_idx", col_dtype),
+            _dev(val, "val", torch.float16), nnz)
+
+
+def spmv_add(row_ptr, col, val, x, y, ws=None, stream=None) -> torch.Tensor:
+    """y += S x in place (col: uint16, or int16 holding the same bits)."""
+    rows = row_ptr.shape[0] - 1
+    x, y, batch, cols = _x_y(x, y, rows)
+    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    rp, ci, cv, nnz = _csr_ptrs(row_ptr, col, val)
+    _check(_lib.sqllm_spmv_add(rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
+                               _dev(y, "y", torch.float16), _dev(ws, "workspace", torch.uint8), ws.numel(),
+                               _stream(stream)), "sqllm_spmv_add")
+    return y
+
+
+def dense_sparse_gemv(packed, lut, bits, row_ptr, col, val, x, y=None, ws=None, stream=None) -> torch.Tensor:
+    """y = (D + S) x in one launch."""
+    rows = lut.shape[0]
+    x, y, batch, cols = _x_y(x, y, rows)
+    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    rp, ci, cv, nnz = _csr_ptrs(row_ptr, col, val)
+    _check(_lib.sqllm_dense_sparse_gemv(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16), bits,
+                                        rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
+                                        _dev(y, "y", torch.float16), _dev(ws, "workspace", torch.uint8), ws.numel(),
+                                        _stream(stream)), "sqllm_dense_sparse_gemv")
+    return y
+
+
+def unpack_codes(packed, rows, cols, bits, stream=None) -> torch.Tensor:
+    """Test-only reader: packed -> uint8 codes [rows, cols] (sqllm_test_unpack)."""
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=packed.device)
+    _check(_lib.sqllm_test_unpack(_dev(packed, "packed", torch.uint8), rows, cols, bits, _dev(out, "codes", torch.uint8),
+                                  _stream(stream)), "sqllm_test_unpack")
+    return out
+
+
+def decode_weights(packed, lut, rows, cols, bits, stream=None) -> torch.Tensor:
+    """Test-only reader: fp16 LUT[r][code[r][c]] [rows, cols] (sqllm_test_decode)."""
+    out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
+    _check(_lib.sqllm_test_decode(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16), rows, cols,
+                                  bits, _dev(out, "w", torch.float16), _stream(stream)), "sqllm_test_decode")
+    return out
+
+
+def set_tuning(waves3: int = 0, waves4: int = 0, target_wgs: int = 0, split: int = 0) -> None:
+    """Test-only: launch configuration of later calls (0 = default)."""
+    _check(_lib.sqllm_test_tuning(waves3, waves4, target_wgs, split), "sqllm_test_tuning")
+
+
+def algorithmic_bytes(rows: int, cols: int, bits: int, nnz: int, batch: int) -> int:
+    """Bytes the product must move once: codes (exactly b bits each), the
+    per-row fp16 tables, the CSR outliers (fp16 value + 16-bit column per
+    nonzero, int32 row pointers), x and y."""
+    b = rows * cols * bits // 8 + rows * (1 << bits) * 2 + 2 * batch * cols + 2 * batch * rows
+    if nnz > 0:
+        b += 4 * nnz + 4 * (rows + 1)
+    return b

@@ -35,9 +35,15 @@
  *   tiles of 64 rows (t = r / 64, lane l = r % 64), groups of 256 columns
  *   (g = c / 256, j = c % 256), 2b pieces of 16 bytes per (row, group).
  *   Piece q of (r, g) sits at byte ((t*G + g)*2b + q)*1024 + l*16, G = cols/256.
- *   The 32b bytes of (r, g), pieces in order, are one little-endian bit
- *   string; code j occupies bits [b*j, b*j + b).  Rows past `rows` in the
- *   last tile are padding.
+ *   The 32b bytes of (r, g), pieces in order, form the group's byte string.
+ *   Codes pair up: pair p holds codes 2p and 2p+1 as
+ *   value = code[2p] | code[2p+1] << b.
+ *   4-bit: byte p of the string is pair p.
+ *   3-bit: the string is 8 units of 12 bytes, unit u holding codes
+ *   32u .. 32u+31 as pairs p = 0..15 of that unit; pair p < 12 is the low
+ *   six bits of unit byte p; pair 12+q (q = 0..3) keeps its bits [2k, 2k+2)
+ *   in the top two bits of unit byte 4k + q, for k = 0, 1, 2.
+ *   Rows past `rows` in the last tile are padding.
  */
 #include <math.h>
 #include <stdint.h>
@@ -115,20 +121,31 @@ static int64_t string_byte_offset(int64_t row, int64_t group, int64_t k, int64_t
     return ((t * G + group) * P + q) * 1024 + l * 16 + m;
 }
 
+/* The b-bit pair value (codes 2p and 2p+1) of pair p (0..127) of (row, group). */
+static unsigned pair_value(const uint8_t *packed, int64_t row, int64_t group, int64_t p, int64_t cols, int bits)
+{
+    if (bits == 4) return packed[string_byte_offset(row, group, p, cols, bits)];
+    int64_t unit = p / 16, pu = p % 16, base = 12 * unit;
+    if (pu < 12) return packed[string_byte_offset(row, group, base + pu, cols, bits)] & 0x3Fu;
+    int64_t q = pu - 12;
+    unsigned v = 0;
+    for (int k = 0; k < 3; ++k) {
+        unsigned byte = packed[string_byte_offset(row, group, base + 4 * k + q, cols, bits)];
+        v |= ((byte >> 6) & 3u) << (2 * k);
+    }
+    return v;
+}
+
 /* Every code of a rows x cols matrix from its packed bytes (uint8 out,
  * row-major). */
 void oracle_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int bits, uint8_t *codes)
 {
-    const int64_t string_bytes = 32 * bits;
+    const unsigned mask = (1u << bits) - 1u;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t c = 0; c < cols; ++c) {
             int64_t g = c / 256, j = c % 256;
-            int64_t p = (int64_t)bits * j;   /* first bit of the code */
-            int64_t k = p / 8, sh = p % 8;
-            unsigned v = packed[string_byte_offset(r, g, k, cols, bits)];
-            if (sh + bits > 8 && k + 1 < string_bytes)
-                v |= (unsigned)packed[string_byte_offset(r, g, k + 1, cols, bits)] << 8;
-            codes[r * cols + c] = (uint8_t)((v >> sh) & ((1u << bits) - 1u));
+            unsigned v = pair_value(packed, r, g, j / 2, cols, bits);
+            codes[r * cols + c] = (uint8_t)((j % 2 ? v >> bits : v) & mask);
         }
     }
 }

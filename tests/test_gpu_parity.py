@@ -1,0 +1,335 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: packing (against a packer written from the layout definition),
+unpacking, decoding, integer-valued products.  Floating point: every output
+within 5e-3 of the oracle's fp64 result, normalised by sum |W||x| of its row
+(rows where the normaliser is 0 must be exactly 0).  Sizes span several
+64-row tiles, several 256-column groups and ragged row tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DevMatrix, assert_close, dev_to_u16, nw, step, u16_to_dev
+from test_oracle_pins import _make_case, pack_from_definition
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ------------------------------------------------------------ pack / unpack
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (63, 512), (65, 256), (130, 768), (257, 1024)])
+def test_pack_bytes_equal_definition(bits, rows, cols):
+    step(f"pack bits={bits} rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows + cols + bits)
+    codes = rng.integers(0, 1 << bits, (rows, cols)).astype(np.uint8)
+    packed = nw().pack(torch.from_numpy(codes).cuda(), bits)
+    torch.cuda.synchronize()
+    want = pack_from_definition(codes, bits)
+    assert packed.numel() == want.size == oracle.packed_bytes(rows, cols, bits)
+    assert np.array_equal(packed.cpu().numpy(), want)
+    # the oracle reads the GPU's bytes back to the same codes
+    assert np.array_equal(oracle.unpack(packed.cpu().numpy(), rows, cols, bits), codes)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (65, 768), (300, 2048)])
+def test_unpack_and_decode_bit_exact(bits, rows, cols):
+    step(f"unpack/decode bits={bits} rows={rows} cols={cols}")
+    rng = np.random.default_rng(7 * rows + cols + bits)
+    codes = rng.integers(0, 1 << bits, (rows, cols)).astype(np.uint8)
+    # tables with subnormals, signed zeros, the largest finite values
+    lut = rng.integers(0, 0x7C00, (rows, 1 << bits)).astype(np.uint16) | (rng.integers(0, 2, (rows, 1 << bits)) << 15).astype(np.uint16)
+    lut[:, 0] = 0x8000
+    lut[:, 1] = 0x0001
+    lut[0, :] = 0x7BFF
+    packed = nw().pack(torch.from_numpy(codes).cuda(), bits)
+    got_codes = nw().unpack_codes(packed, rows, cols, bits)
+    got_w = nw().decode_weights(packed, u16_to_dev(lut), rows, cols, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(got_codes.cpu().numpy(), codes)
+    assert np.array_equal(dev_to_u16(got_w), oracle.decode(codes, lut, bits))
+
+
+def test_pack_rejects_out_of_range_code():
+    step("pack code range")
+    codes = np.zeros((64, 256), np.uint8)
+    codes[10, 100] = 8
+    with pytest.raises(nw().SqllmError) as e:
+        nw().pack(torch.from_numpy(codes).cuda(), 3)
+    assert e.value.status == 6
+    codes[10, 100] = 16
+    with pytest.raises(nw().SqllmError):
+        nw().pack(torch.from_numpy(codes).cuda(), 4)
+    codes[10, 100] = 15
+    nw().pack(torch.from_numpy(codes).cuda(), 4)
+
+
+# ------------------------------------------------------------ products, small shapes
+
+SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8), (300, 4096, 1)]
+SPARSITY = ["none", "one", "5pct", "50pct", "full", "empty_rows", "dense_row"]
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rows,cols,batch", SHAPES)
+@pytest.mark.parametrize("sparsity", SPARSITY)
+def test_fused_matches_oracle(bits, rows, cols, batch, sparsity):
+    step(f"fused bits={bits} rows={rows} cols={cols} batch={batch} sparsity={sparsity}")
+    rng = np.random.default_rng(hash((bits, rows, cols, batch, sparsity)) % 2**32)
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, sparsity)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y = d.fused()
+    torch.cuda.synchronize()
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    assert_close(y, y_ref, scale, TOL, "fused")
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rows,cols,batch", SHAPES)
+def test_gemv_matches_oracle(bits, rows, cols, batch):
+    step(f"gemv bits={bits} rows={rows} cols={cols} batch={batch}")
+    rng = np.random.default_rng(hash((bits, rows, cols, batch, "gemv")) % 2**32)
+    codes, lut, x, _, _, _ = _make_case(rng, rows, cols, bits, batch, "none")
+    d = DevMatrix(codes, lut, bits, None, None, None, x)
+    y = d.gemv()
+    torch.cuda.synchronize()
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    assert_close(y, y_ref, scale, TOL, "gemv")
+
+
+@pytest.mark.parametrize("rows,cols,batch", SHAPES)
+@pytest.mark.parametrize("sparsity", ["one", "5pct", "full", "empty_rows", "dense_row"])
+def test_spmv_add_matches_oracle(rows, cols, batch, sparsity):
+    step(f"spmv_add rows={rows} cols={cols} batch={batch} sparsity={sparsity}")
+    rng = np.random.default_rng(hash((rows, cols, batch, sparsity, "spmv")) % 2**32)
+    _, _, x, rp, col, val = _make_case(rng, rows, cols, 3, batch, sparsity)
+    y_in = (rng.standard_normal((batch, rows)) * 0.5).astype(np.float16).view(np.uint16)
+    codes = np.zeros((rows, cols), np.uint8)
+    d = DevMatrix(codes, np.zeros((rows, 8), np.uint16), 3, rp, col, val, x)
+    y = u16_to_dev(y_in.copy())
+    d.spmv_add(y)
+    torch.cuda.synchronize()
+    y_ref, scale = oracle.spmv_add(rp, col, val, x, y_in, rows)
+    assert_close(y, y_ref, scale, TOL, "spmv_add")
+
+
+def test_spmv_add_without_outliers_is_noop():
+    step("spmv_add nnz=0")
+    rows, cols = 70, 512
+    x = u16_to_dev(np.zeros((1, cols), np.uint16))
+    y0 = (np.arange(rows, dtype=np.float64) / 7).astype(np.float16).view(np.uint16)[None, :]
+    y = u16_to_dev(y0.copy())
+    nw().spmv_add(torch.zeros(rows + 1, dtype=torch.int32, device="cuda"), None, None, x, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_u16(y), y0)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_stream_ordered_pair_equals_fused(bits):
+    step(f"gemv+spmv_add vs fused bits={bits}")
+    rng = np.random.default_rng(31 + bits)
+    rows, cols, batch = 257, 2048, 2
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "5pct")
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y2 = d.gemv()
+    d.spmv_add(y2)
+    y1 = d.fused()
+    torch.cuda.synchronize()
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    assert_close(y1, y_ref, scale, TOL, "fused")
+    assert_close(y2, y_ref, scale, TOL, "stream-ordered")
+
+
+def _integer_case(rng, rows, cols, bits, batch, dense_max=2, sparse_max=4, density=0.05):
+    codes = rng.integers(0, 1 << bits, (rows, cols)).astype(np.uint8)
+    lut = rng.integers(-dense_max, dense_max + 1, (rows, 1 << bits)).astype(np.float16).view(np.uint16)
+    x = rng.integers(-2, 3, (batch, cols)).astype(np.float16).view(np.uint16)
+    mask = rng.random((rows, cols)) < density
+    rp = np.zeros(rows + 1, np.int32)
+    rp[1:] = np.cumsum(mask.sum(axis=1))
+    col = np.nonzero(mask)[1].astype(np.uint16)
+    val = rng.integers(-sparse_max, sparse_max + 1, col.size).astype(np.float16).view(np.uint16)
+    return codes, lut, x, rp, col, val
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rows,cols,batch", [(65, 768, 1), (300, 4096, 3), (130, 22016, 1)])
+def test_integer_inputs_bit_exact(bits, rows, cols, batch):
+    """Integer LUT, x and outliers: every fp32 partial sum is an exact integer,
+    so the single fp16 rounding of the fused call is determined."""
+    step(f"integer fused bits={bits} rows={rows} cols={cols} batch={batch}")
+    rng = np.random.default_rng(rows * cols + bits)
+    codes, lut, x, rp, col, val = _integer_case(rng, rows, cols, bits, batch)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y = d.fused()
+    yg = d.gemv()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    assert np.array_equal(dev_to_u16(y), oracle.f64_array_to_f16(y_ref))
+    yd_ref, _ = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    assert np.array_equal(dev_to_u16(yg), oracle.f64_array_to_f16(yd_ref))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_integer_stream_ordered_bit_exact(bits):
+    """With |D x| <= 2048 the intermediate fp16 is exact, so gemv followed by
+    spmv_add rounds to the same bits as the fused call."""
+    step(f"integer stream-ordered bits={bits}")
+    rng = np.random.default_rng(5 + bits)
+    rows, cols, batch = 200, 256, 2
+    codes, lut, x, rp, col, val = _integer_case(rng, rows, cols, bits, batch, dense_max=2, density=0.1)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y = d.gemv()
+    d.spmv_add(y)
+    yf = d.fused()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    want = oracle.f64_array_to_f16(y_ref)
+    assert np.array_equal(dev_to_u16(y), want)
+    assert np.array_equal(dev_to_u16(yf), want)
+
+
+def test_subnormal_inputs_are_not_flushed():
+    """Tables of fp16 subnormals times small-integer activations: exact
+    results of a few units of 2^-24, which a flush to zero would lose."""
+    step("subnormals")
+    rng = np.random.default_rng(77)
+    rows, cols, bits = 130, 512, 3
+    codes = rng.integers(0, 8, (rows, cols)).astype(np.uint8)
+    lut = rng.integers(0, 4, (rows, 8)).astype(np.uint16)  # 0..3 units of 2^-24
+    lut |= (rng.integers(0, 2, (rows, 8)) << 15).astype(np.uint16)
+    x = np.zeros((1, cols), np.uint16)
+    x[0, rng.choice(cols, 6, replace=False)] = np.float16(1.0).view(np.uint16)
+    d = DevMatrix(codes, lut, bits, None, None, None, x)
+    y = d.fused()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    assert np.any(y_ref != 0)
+    assert np.array_equal(dev_to_u16(y), oracle.f64_array_to_f16(y_ref))
+
+
+def test_batch_equals_separate_calls():
+    step("batch 8 vs 8 x batch 1")
+    rng = np.random.default_rng(3)
+    rows, cols, bits = 257, 2048, 3
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, 8, "5pct")
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y8 = d.fused()
+    singles = []
+    for b in range(8):
+        db = DevMatrix(codes, lut, bits, rp, col, val, x[b:b + 1])
+        singles.append(db.fused())
+    torch.cuda.synchronize()
+    y8 = dev_to_u16(y8)
+    for b in range(8):
+        assert np.array_equal(y8[b], dev_to_u16(singles[b])[0])
+
+
+def test_repeated_calls_are_bit_identical():
+    step("determinism")
+    rng = np.random.default_rng(4)
+    codes, lut, x, rp, col, val = _make_case(rng, 300, 4096, 3, 2, "dense_row")
+    d = DevMatrix(codes, lut, 3, rp, col, val, x)
+    outs = [dev_to_u16(d.fused()) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_permuted_table_with_remapped_codes():
+    """Permuting a row's table entries together with its codes leaves y unchanged."""
+    step("lut permutation invariance")
+    rng = np.random.default_rng(9)
+    rows, cols, bits = 130, 1024, 4
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, 1, "5pct")
+    perm = rng.permutation(16)
+    inv = np.argsort(perm)
+    lut2 = lut[:, perm]          # entry j of the new table = old entry perm[j]
+    codes2 = inv[codes].astype(np.uint8)
+    y1 = DevMatrix(codes, lut, bits, rp, col, val, x).fused()
+    y2 = DevMatrix(codes2, lut2, bits, rp, col, val, x).fused()
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_u16(y1), dev_to_u16(y2))
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace serves consecutive calls of different shapes on a stream."""
+    step("workspace reuse")
+    rng = np.random.default_rng(10)
+    ws = torch.zeros(nw().workspace_bytes(22016, 8192, 2), dtype=torch.uint8, device="cuda")
+    cases = []
+    for rows, cols, batch in [(4096, 8192, 1), (130, 2048, 2), (22016, 8192, 1), (1000, 4096, 1), (8192, 4096, 2),
+                              (22016, 4096, 1)]:
+        codes, lut, x, rp, col, val = _make_case(rng, rows, cols, 3, batch, "5pct")
+        d = DevMatrix(codes, lut, 3, rp, col, val, x)
+        cases.append((d.fused(ws=ws), codes, lut, x, rp, col, val))
+    torch.cuda.synchronize()
+    for y, codes, lut, x, rp, col, val in cases:
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+        assert_close(y, y_ref, scale, TOL, "shared workspace")
+    # the arrival counters (last 4 * tiles bytes) are back to zero
+    assert int(ws[-4 * 344:].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("waves,split", [(1, 1), (1, 8), (2, 3), (4, 1), (4, 16), (8, 2), (8, 7)])
+def test_launch_configurations(bits, waves, split):
+    """Every waves-per-workgroup / column-split combination gives the same
+    answer (one wave per workgroup included)."""
+    step(f"launch config bits={bits} waves={waves} split={split}")
+    rng = np.random.default_rng(waves * 100 + split + bits)
+    rows, cols, batch = 193, 4096, 2
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "dense_row")
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    try:
+        nw().set_tuning(waves3=waves, waves4=waves, split=split)
+        y = d.fused()
+        yg = d.gemv()
+        ys = d.spmv_add(yg.clone())
+        torch.cuda.synchronize()
+    finally:
+        nw().set_tuning()
+    assert_close(y, y_ref, scale, TOL, "fused")
+    assert_close(ys, y_ref, scale, TOL, "stream-ordered")
+
+
+# ------------------------------------------------------------ the evaluation workloads
+
+def _check_matrix(m: synth.Matrix, sel=None, ws=None):
+    d = DevMatrix.from_synth(m)
+    y = d.fused(ws=ws)
+    torch.cuda.synchronize()
+    if sel is None:
+        y_ref, scale = oracle.dense_sparse_gemv(m.codes, m.lut, m.spec.bits, m.row_ptr, m.col, m.val, m.x)
+        return assert_close(y, y_ref, scale, TOL, m.spec.name)
+    sel = np.asarray(sel)
+    y_ref, scale = oracle.dense_sparse_gemv(m.codes[sel], m.lut, m.spec.bits, m.row_ptr, m.col, m.val, m.x,
+                                            rows=m.spec.rows, sel=sel)
+    return assert_close(y[:, torch.from_numpy(sel).cuda()], y_ref, scale, TOL, m.spec.name)
+
+
+@pytest.mark.parametrize("workload", [1, 2, 3])
+def test_workload_full(workload):
+    for i, spec in enumerate(synth.workload(workload)):
+        step(f"workload {workload} matrix {i} {spec}")
+        m = synth.make_matrix(spec, seed=0, workload=workload, index=i)
+        _check_matrix(m)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_workload4(batch):
+    rng = np.random.default_rng(batch)
+    for i, spec in enumerate(synth.workload(4, batch=batch)):
+        step(f"workload 4 batch {batch} matrix {i} {spec}")
+        m = synth.make_matrix(spec, seed=0, workload=4, index=i)
+        sel = None if batch == 1 else np.sort(rng.choice(spec.rows, 2048, replace=False))
+        _check_matrix(m, sel)

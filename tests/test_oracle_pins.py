@@ -97,18 +97,36 @@ def test_packed_bytes_formula():
     assert oracle.packed_bytes(22016, 8192, 3) == 22016 * 8192 * 3 // 8
 
 
+def group_string(codes_row_group: np.ndarray, bits: int) -> bytes:
+    """The 32*bits-byte string of one (row, 256-column group), from the layout
+    definition: pairs p = code[2p] | code[2p+1] << bits; 4-bit: byte p is
+    pair p; 3-bit: units of 12 bytes / 16 pairs, pair p < 12 in the low six
+    bits of unit byte p, pair 12+q spread two bits at a time over the top two
+    bits of unit bytes q, 4+q, 8+q."""
+    c = [int(v) for v in codes_row_group]
+    pairs = [c[2 * p] | (c[2 * p + 1] << bits) for p in range(128)]
+    if bits == 4:
+        return bytes(pairs)
+    out = bytearray(96)
+    for u in range(8):
+        unit = pairs[16 * u:16 * u + 16]
+        for p in range(12):
+            out[12 * u + p] |= unit[p]
+        for q in range(4):
+            for k in range(3):
+                out[12 * u + 4 * k + q] |= ((unit[12 + q] >> (2 * k)) & 3) << 6
+    return bytes(out)
+
+
 def pack_from_definition(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Packer written from the layout definition with Python big integers."""
+    """Packer written here from the layout definition (Python integers)."""
     rows, cols = codes.shape
     T, G, P = (rows + 63) // 64, cols // 256, 2 * bits
     buf = np.zeros(T * G * P * 1024, dtype=np.uint8)
     for r in range(rows):
         t, l = divmod(r, 64)
         for g in range(G):
-            s = 0
-            for j in range(256):
-                s |= int(codes[r, 256 * g + j]) << (bits * j)
-            string = s.to_bytes(32 * bits, "little")
+            string = group_string(codes[r, 256 * g:256 * g + 256], bits)
             for q in range(P):
                 off = ((t * G + g) * P + q) * 1024 + l * 16
                 buf[off:off + 16] = np.frombuffer(string[16 * q:16 * q + 16], dtype=np.uint8)

@@ -43,15 +43,14 @@ MUTANTS = {
     "row_contiguous_layout": (
         "return ((t * G + group) * P + q) * 1024 + l * 16 + m;",
         "return ((t * G + group) * 64 + l) * (16 * P) + q * 16 + m;"),
-    "big_endian_bit_string": (
-        "unsigned v = packed[string_byte_offset(r, g, k, cols, bits)];\n"
-        "            if (sh + bits > 8 && k + 1 < string_bytes)\n"
-        "                v |= (unsigned)packed[string_byte_offset(r, g, k + 1, cols, bits)] << 8;\n"
-        "            codes[r * cols + c] = (uint8_t)((v >> sh) & ((1u << bits) - 1u));",
-        "unsigned v = packed[string_byte_offset(r, g, k, cols, bits)];\n"
-        "            if (sh + bits > 8 && k + 1 < string_bytes)\n"
-        "                v |= (unsigned)packed[string_byte_offset(r, g, k + 1, cols, bits)] << 8;\n"
-        "            codes[r * cols + c] = (uint8_t)((v >> (8 - sh - bits < 0 ? 0 : 8 - sh - bits)) & ((1u << bits) - 1u));"),
+    "extra_pair_bits_reversed": (
+        "v |= ((byte >> 6) & 3u) << (2 * k);", "v |= ((byte >> 6) & 3u) << (4 - 2 * k);"),
+    "nibbles_swapped": (
+        "codes[r * cols + c] = (uint8_t)((j % 2 ? v >> bits : v) & mask);",
+        "codes[r * cols + c] = (uint8_t)((j % 2 ? v : v >> bits) & mask);"),
+    "extra_pairs_unit_stride": (
+        "int64_t unit = p / 16, pu = p % 16, base = 12 * unit;",
+        "int64_t unit = p / 16, pu = p % 16, base = 16 * unit;"),
     "normaliser_without_abs": (
         "sc += fabs(w[c]) * fabs(oracle_f16_to_f64(xb[c]));", "sc += w[c] * oracle_f16_to_f64(xb[c]);"),
 }
