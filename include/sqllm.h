@@ -29,7 +29,7 @@
  *   - fp16 values are passed as raw IEEE binary16 bit patterns (uint16_t).
  *   - Layouts are row-major and contiguous:
  *       lut  [rows][2^bits]          16-byte aligned
- *       x    [batch][cols]           4-byte aligned
+ *       x    [batch][cols]           16-byte aligned
  *       y    [batch][rows]           4-byte aligned
  *       row_ptr [rows+1] int32, col_idx [nnz] uint16, val [nnz] fp16
  *     i.e. y = x W^T with W = [rows][cols] = out x in features.
@@ -56,16 +56,20 @@
  *   Total size: sqllm_packed_bytes() = ceil(rows / 64) * 64 * cols * b / 8.
  *   The packed buffer must be 16-byte aligned.
  *
- * Workspace: the hot calls split long rows across workgroups and combine
- * the fp32 partial sums on the device.  They take a caller-owned workspace
- * of at least sqllm_workspace_bytes(rows, cols, batch) bytes (a multiple of
- * 4), 256-byte aligned, ZERO-FILLED before its first use.  Partial sums are
- * kept from its start and one arrival counter per 64-row tile in its last
- * 4 * ceil(rows / 64) bytes.  Every call leaves it ready for the next one
- * (its counters return to zero when the call's kernel ends), so one
- * workspace can serve any sequence of calls, of any shapes it is large
- * enough for, that are ordered on one stream.  Calls that may run
- * concurrently need separate workspaces.
+ * Workspace: the hot calls may split a row's columns over several
+ * workgroups, which then combine their fp32 partial sums on the device.
+ * They take a caller-owned workspace of at least
+ * sqllm_workspace_bytes(rows, cols, batch) bytes, 256-byte aligned,
+ * ZERO-FILLED before its first use: one 8-byte (fp32 sum, count) word per
+ * output, which the workgroup completing an output resets to zero.  Every
+ * call therefore leaves it ready for the next one, so one workspace serves
+ * any sequence of calls, of any shapes it is large enough for, that are
+ * ordered on one stream.  Calls that may run concurrently need separate
+ * workspaces.  When a call does not split (small shapes) the workspace may
+ * be NULL.  Results are bit-identical run to run whenever a row's columns
+ * are split over at most two workgroups (all shapes up to 22016 x 22016 with
+ * the built-in launch shapes); beyond that the fp32 partial sums are added
+ * in arrival order.
  */
 #ifndef SQLLM_H
 #define SQLLM_H
@@ -163,14 +167,15 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
  */
 sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, int bits, uint8_t *codes,
                                hipStream_t stream);
-/*   sqllm_test_tuning: set the launch configuration of later calls in this
- *   process: waves per workgroup for 3-bit and 4-bit codes (1..8), the
- *   workgroup count the column split aims for, and a forced split
- *   (1..16).  0 restores a value's default (environment SQLLM_WAVES_3,
- *   SQLLM_WAVES_4, SQLLM_TARGET_WGS, SQLLM_SPLIT, else built in).  Results
- *   agree within the stated tolerance for every configuration; not
- *   thread-safe against concurrent calls. */
-sqllm_status sqllm_test_tuning(int waves3, int waves4, int target_wgs, int split);
+/*   sqllm_test_tuning: launch shape of later calls in this process: the
+ *   workgroup count the column split aims for, the fewest 256-column groups
+ *   per workgroup, a forced split (1..64) and forced waves per workgroup
+ *   (1..16).  0 restores a value's default (environment SQLLM_TARGET_WGS,
+ *   SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES, else built in).  Shapes that no
+ *   compiled kernel fits fail with SQLLM_ERR_SHAPE.  Results agree within the
+ *   stated tolerance for every shape; not thread-safe against concurrent
+ *   calls. */
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves);
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
                                uint16_t *w, hipStream_t stream);
 

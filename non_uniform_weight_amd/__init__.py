@@ -200,9 +200,9 @@ def decode_weights(packed, lut, rows, cols, bits, stream=None) -> torch.Tensor:
     return out
 
 
-def set_tuning(waves3: int = 0, waves4: int = 0, target_wgs: int = 0, split: int = 0) -> None:
-    """Test-only: launch configuration of later calls (0 = default)."""
-    _check(_lib.sqllm_test_tuning(waves3, waves4, target_wgs, split), "sqllm_test_tuning")
+def set_tuning(target_wgs: int = 0, min_gps: int = 0, split: int = 0, waves: int = 0) -> None:
+    """Test-only: launch shape of later calls (0 = default)."""
+    _check(_lib.sqllm_test_tuning(target_wgs, min_gps, split, waves), "sqllm_test_tuning")
 
 
 def algorithmic_bytes(rows: int, cols: int, bits: int, nnz: int, batch: int) -> int:

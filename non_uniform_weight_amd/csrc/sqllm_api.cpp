@@ -1,6 +1,6 @@
 // sqllm_api.cpp -- the C ABI declared in include/sqllm.h: argument checks
-// (all done on the host before any HIP call), the split heuristic, and the
-// kernel launches on the caller's stream.
+// (all done on the host before any HIP call), the choice of launch shape,
+// and the kernel launches on the caller's stream.
 #include "sqllm.h"
 
 #include <stdint.h>
@@ -12,13 +12,16 @@ using namespace sqllm;
 
 namespace {
 
-// Tuning knobs (environment, read once): SQLLM_WAVES_3 / SQLLM_WAVES_4 set
-// the waves per workgroup of the dense kernels, SQLLM_TARGET_WGS the
-// workgroup count the column split aims for, SQLLM_SPLIT forces a split.
+// Launch-shape knobs.  Defaults are built in; the environment (read once:
+// SQLLM_TARGET_WGS, SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES) or
+// sqllm_test_tuning() may override them.  Every value gives the same result
+// within the stated tolerance (bit-identical while split <= 2).
 struct Tuning {
-    int waves3 = 4, waves4 = 8, waves_sparse = 4;
-    int target_wgs = 1024;
-    int force_split = 0;
+    int target_wgs = 256;   // workgroups the column split aims for (one per compute unit)
+    int min_gps = 8;        // fewest column groups per workgroup (pair-table build amortisation)
+    int force_split = 0;    // 0: choose; else workgroups per row tile
+    int force_waves = 0;    // 0: choose; else waves per workgroup
+    int sparse_waves = 8;   // waves per workgroup of the outlier-only kernel
     Tuning()
     {
         auto get = [](const char *name, int lo, int hi, int dflt) {
@@ -27,10 +30,10 @@ struct Tuning {
             long x = strtol(v, nullptr, 10);
             return (x < lo || x > hi) ? dflt : (int)x;
         };
-        waves3 = get("SQLLM_WAVES_3", 1, kMaxWaves, waves3);
-        waves4 = get("SQLLM_WAVES_4", 1, kMaxWaves, waves4);
         target_wgs = get("SQLLM_TARGET_WGS", 1, 1 << 20, target_wgs);
-        force_split = get("SQLLM_SPLIT", 1, kSplitCap, 0);
+        min_gps = get("SQLLM_MIN_GPS", 1, 1 << 16, min_gps);
+        force_split = get("SQLLM_SPLIT", 1, kMaxSplit, 0);
+        force_waves = get("SQLLM_WAVES", 1, kMaxWaves, 0);
     }
 };
 
@@ -53,47 +56,93 @@ sqllm_status check_shape(int64_t rows, int64_t cols)
     return SQLLM_OK;
 }
 
-// Workspace layout: fp32 partial sums from the start, one arrival counter per
-// row tile in the LAST 4 * tiles bytes.  Counters of calls with different
-// tile counts overlap only each other (all zero between calls) and never the
-// partial sums of any call the workspace is large enough for.
+// One 8-byte (fp32 sum, count) word per (tile, batch column, row of tile).
 size_t workspace_need(int64_t rows, int batch)
 {
-    const int64_t tiles = tiles_of(rows);
-    return (size_t)tiles * 4 + (size_t)tiles * kSplitCap * (size_t)batch * kTileRows * sizeof(float);
+    return (size_t)tiles_of(rows) * (size_t)batch * kTileRows * 8;
 }
 
-// Column split: enough workgroups to fill the chip, at least one 256-column
-// group per wave.
-void choose_split_dense(int64_t tiles, int64_t groups, int waves, int *split, int *gps)
+// Waves per workgroup and compiled groups-per-wave for gps groups; false if
+// no compiled kernel fits.
+bool fit_waves(int gps, int bits, int batch, int *waves, int *gw)
 {
+    for (int g = 1; g <= 4; ++g) {
+        int w = (gps + g - 1) / g;
+        if (tuning().force_waves) {
+            w = tuning().force_waves;
+            if ((int64_t)w * g < gps) continue;
+        }
+        if (w <= max_waves(bits, batch, g)) {
+            *waves = w;
+            *gw = g;
+            return true;
+        }
+    }
+    return false;
+}
+
+// Column split and workgroup shape for the dense modes: about target_wgs
+// workgroups, at least min_gps groups each, a wave's codes in registers,
+// everything within the LDS of one compute unit.
+bool choose_dense(KernelArgs &a, int bits, int batch, bool sparse, LaunchShape &ls)
+{
+    const int64_t T = a.tiles, G = a.groups;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        s = (tuning().target_wgs + tiles - 1) / tiles;
-        int64_t cap = groups / waves;
+        s = (tuning().target_wgs + T - 1) / T;
+        int64_t cap = G / tuning().min_gps;
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
     }
-    if (s > kSplitCap) s = kSplitCap;
-    if (s > groups) s = groups;
+    if (s > G) s = G;
     if (s < 1) s = 1;
-    int64_t g = (groups + s - 1) / s;
-    s = (groups + g - 1) / g; // no empty splits
-    *split = (int)s;
-    *gps = (int)g;
+    for (; s <= G && s <= kMaxSplit; ++s) {
+        const int gps = (int)((G + s - 1) / s);
+        const int split = (int)((G + gps - 1) / gps); // no empty splits
+        int waves = 0, gw = 0;
+        if (!fit_waves(gps, bits, batch, &waves, &gw)) continue;
+        // x staged in LDS: the workgroup's columns, or all of them when that
+        // fits and outliers need it (their columns are anywhere in the row)
+        int x_full = split == 1;
+        size_t dyn = dynamic_lds_bytes(gps, batch, waves, sparse);
+        if (sparse && split > 1) {
+            const size_t full = dynamic_lds_bytes((int)G, batch, waves, true);
+            if (kTableBytes + full <= (size_t)kLdsBudget) {
+                x_full = 1;
+                dyn = full;
+            }
+        }
+        if (kTableBytes + dyn > (size_t)kLdsBudget) continue;
+        a.split = split;
+        a.gps = gps;
+        a.gpw = (gps + waves - 1) / waves;
+        a.x_full = x_full;
+        ls.waves = waves;
+        ls.gw = gw;
+        ls.dyn_lds = dyn;
+        return true;
+    }
+    return false;
 }
 
-// Outlier-only split: about 2048 nonzeros per workgroup on average.
-int choose_split_sparse(int64_t tiles, int64_t nnz)
+// Outlier-only kernel: about 256 nonzeros per wave on average.
+void choose_sparse(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
 {
+    const int waves = tuning().force_waves ? tuning().force_waves : tuning().sparse_waves;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        const int64_t per_tile = (nnz + tiles - 1) / tiles;
-        s = (per_tile + 2047) / 2048;
+        const int64_t per_tile = (nnz + a.tiles - 1) / a.tiles;
+        s = (per_tile + waves * 256 - 1) / (waves * 256);
     }
-    if (s > kSplitCap) s = kSplitCap;
+    if (s > kMaxSplit) s = kMaxSplit;
     if (s < 1) s = 1;
-    return (int)s;
+    a.split = (int)s;
+    a.gps = 0;
+    a.gpw = 0;
+    ls.waves = waves;
+    ls.gw = 1;
+    a.x_full = 0; // outlier gathers read x from global memory (L2)
+    ls.dyn_lds = dynamic_lds_bytes(0, batch, waves, true);
 }
 
 sqllm_status common_checks(int64_t rows, int64_t cols, const uint16_t *x, int batch, const uint16_t *y)
@@ -102,7 +151,7 @@ sqllm_status common_checks(int64_t rows, int64_t cols, const uint16_t *x, int ba
     sqllm_status st = check_shape(rows, cols);
     if (st != SQLLM_OK) return st;
     if (batch < 1 || batch > kMaxBatch) return SQLLM_ERR_BATCH;
-    if (!aligned(x, 4) || !aligned(y, 4)) return SQLLM_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(y, 4)) return SQLLM_ERR_ALIGN;
     return SQLLM_OK;
 }
 
@@ -121,15 +170,21 @@ sqllm_status sparse_checks(const int32_t *row_ptr, const uint16_t *col_idx, cons
 sqllm_status workspace_checks(int split, int64_t rows, int batch, void *ws, size_t ws_bytes)
 {
     if (split <= 1) return SQLLM_OK;
-    if (!ws || !aligned(ws, 256) || ws_bytes % 4 != 0 || ws_bytes < workspace_need(rows, batch))
-        return SQLLM_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256) || ws_bytes < workspace_need(rows, batch)) return SQLLM_ERR_WORKSPACE;
     return SQLLM_OK;
 }
 
-void attach_workspace(KernelArgs &a, void *ws, size_t ws_bytes)
+KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y, void *ws)
 {
-    a.part = (float *)ws;
-    a.counters = ws ? (uint32_t *)((char *)ws + ws_bytes) - a.tiles : nullptr;
+    KernelArgs a{};
+    a.x = x;
+    a.y = y;
+    a.slots = (unsigned long long *)ws;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.tiles = (int)tiles_of(rows);
+    a.groups = (int)(cols / kGroupCols);
+    return a;
 }
 
 } // namespace
@@ -204,25 +259,19 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     if (st != SQLLM_OK) return st;
     if (!aligned(packed, 16) || !aligned(lut, 16)) return SQLLM_ERR_ALIGN;
 
-    KernelArgs a{};
+    KernelArgs a = base_args(rows, cols, x, y, workspace);
     a.packed = packed;
     a.lut = lut;
     a.row_ptr = row_ptr;
     a.col = col_idx;
     a.val = val;
-    a.x = x;
-    a.y = y;
-    a.rows = (int)rows;
-    a.cols = (int)cols;
-    a.tiles = (int)tiles_of(rows);
-    a.groups = (int)(cols / kGroupCols);
-    const int waves = bits == 3 ? tuning().waves3 : tuning().waves4;
-    choose_split_dense(a.tiles, a.groups, waves, &a.split, &a.gps);
+    const bool sparse = nnz > 0;
+    LaunchShape ls{};
+    if (!choose_dense(a, bits, batch, sparse, ls)) return SQLLM_ERR_SHAPE;
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
-    attach_workspace(a, workspace, workspace_bytes);
-    const bool sparse = nnz > 0;
-    if (launch_dense_sparse(a, bits, batch, true, sparse, false, waves, stream) != hipSuccess) return SQLLM_ERR_HIP;
+    if (launch_dense_sparse(a, bits, batch, sparse ? kFused : kDenseOnly, ls, stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }
 
@@ -236,35 +285,27 @@ sqllm_status sqllm_spmv_add(const int32_t *row_ptr, const uint16_t *col_idx, con
     if (st != SQLLM_OK) return st;
     if (nnz == 0) return SQLLM_OK;
 
-    KernelArgs a{};
+    KernelArgs a = base_args(rows, cols, x, y, workspace);
     a.row_ptr = row_ptr;
     a.col = col_idx;
     a.val = val;
-    a.x = x;
-    a.y = y;
-    a.rows = (int)rows;
-    a.cols = (int)cols;
-    a.tiles = (int)tiles_of(rows);
-    a.groups = (int)(cols / kGroupCols);
-    a.split = choose_split_sparse(a.tiles, nnz);
-    a.gps = 0;
+    LaunchShape ls{};
+    choose_sparse(a, batch, nnz, ls);
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
-    attach_workspace(a, workspace, workspace_bytes);
-    if (launch_dense_sparse(a, 3, batch, false, true, true, tuning().waves_sparse, stream) != hipSuccess)
-        return SQLLM_ERR_HIP;
+    if (launch_dense_sparse(a, 3, batch, kSparseAdd, ls, stream) != hipSuccess) return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }
 
-sqllm_status sqllm_test_tuning(int waves3, int waves4, int target_wgs, int split)
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves)
 {
     const Tuning dflt;
-    if (waves3 > kMaxWaves || waves4 > kMaxWaves || split > kSplitCap) return SQLLM_ERR_SHAPE;
+    if (split > kMaxSplit || waves > kMaxWaves) return SQLLM_ERR_SHAPE;
     Tuning &t = tuning_state();
-    t.waves3 = waves3 > 0 ? waves3 : dflt.waves3;
-    t.waves4 = waves4 > 0 ? waves4 : dflt.waves4;
     t.target_wgs = target_wgs > 0 ? target_wgs : dflt.target_wgs;
+    t.min_gps = min_gps > 0 ? min_gps : dflt.min_gps;
     t.force_split = split > 0 ? split : dflt.force_split;
+    t.force_waves = waves > 0 ? waves : dflt.force_waves;
     return SQLLM_OK;
 }
 

@@ -1,0 +1,11 @@
+// sqllm_fused3.hip -- instantiations of the 3-bit fused kernels (y = (D + S) x).
+#include "sqllm_device.h"
+
+namespace sqllm {
+
+hipError_t launch_fused3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_gw<3, kFused>(a, batch, ls, stream);
+}
+
+} // namespace sqllm

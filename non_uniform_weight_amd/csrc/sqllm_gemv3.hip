@@ -1,0 +1,11 @@
+// sqllm_gemv3.hip -- instantiations of the 3-bit gemv kernels (y = D x).
+#include "sqllm_device.h"
+
+namespace sqllm {
+
+hipError_t launch_gemv3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_gw<3, kDenseOnly>(a, batch, ls, stream);
+}
+
+} // namespace sqllm

@@ -1,0 +1,11 @@
+// sqllm_gemv4.hip -- instantiations of the 4-bit gemv kernels (y = D x).
+#include "sqllm_device.h"
+
+namespace sqllm {
+
+hipError_t launch_gemv4(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_gw<4, kDenseOnly>(a, batch, ls, stream);
+}
+
+} // namespace sqllm

@@ -83,6 +83,7 @@ def test_gemv_argument_errors(lib):
     assert gemv(lib, batch=0) == 4
     assert gemv(lib, batch=9) == 4
     assert gemv(lib, x=MIS) == 5
+    assert gemv(lib, x=P(0x200008)) == 5                 # x must be 16-byte aligned
     assert gemv(lib, y=P(0x200001)) == 5
     assert gemv(lib, packed=P(0x100008)) == 5
     assert gemv(lib, lut=P(0x100004)) == 5
@@ -121,8 +122,8 @@ def test_pack_and_reader_argument_errors(lib):
 
 
 def test_tuning_hook_bounds(lib):
-    assert lib.sqllm_test_tuning(9, 0, 0, 0) == 3
-    assert lib.sqllm_test_tuning(0, 0, 0, 17) == 3
+    assert lib.sqllm_test_tuning(0, 0, 65, 0) == 3      # split above 64
+    assert lib.sqllm_test_tuning(0, 0, 0, 17) == 3      # more than 16 waves
     assert lib.sqllm_test_tuning(0, 0, 0, 0) == 0
 
 

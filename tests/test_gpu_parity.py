@@ -275,23 +275,23 @@ def test_workspace_shared_across_shapes():
     for y, codes, lut, x, rp, col, val in cases:
         y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
         assert_close(y, y_ref, scale, TOL, "shared workspace")
-    # the arrival counters (last 4 * tiles bytes) are back to zero
-    assert int(ws[-4 * 344:].view(torch.int32).abs().sum().item()) == 0
+    # every (sum, count) word was reset by the workgroup that completed it
+    assert int(ws.view(torch.int32).abs().sum().item()) == 0
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-@pytest.mark.parametrize("waves,split", [(1, 1), (1, 8), (2, 3), (4, 1), (4, 16), (8, 2), (8, 7)])
-def test_launch_configurations(bits, waves, split):
-    """Every waves-per-workgroup / column-split combination gives the same
+@pytest.mark.parametrize("split,waves", [(1, 1), (1, 16), (2, 8), (3, 5), (7, 2), (16, 1), (0, 0)])
+def test_launch_configurations(bits, split, waves):
+    """Column splits and waves per workgroup of every kind give the same
     answer (one wave per workgroup included)."""
-    step(f"launch config bits={bits} waves={waves} split={split}")
+    step(f"launch config bits={bits} split={split} waves={waves}")
     rng = np.random.default_rng(waves * 100 + split + bits)
     rows, cols, batch = 193, 4096, 2
     codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "dense_row")
     y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
     d = DevMatrix(codes, lut, bits, rp, col, val, x)
     try:
-        nw().set_tuning(waves3=waves, waves4=waves, split=split)
+        nw().set_tuning(split=split, waves=waves)
         y = d.fused()
         yg = d.gemv()
         ys = d.spmv_add(yg.clone())
