@@ -13,15 +13,14 @@ using namespace sqllm;
 namespace {
 
 // Launch-shape knobs.  Defaults are built in; the environment (read once:
-// SQLLM_TARGET_WGS, SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES) or
-// sqllm_test_tuning() may override them.  Every value gives the same result
-// within the stated tolerance (bit-identical while split <= 2).
+// SQLLM_TARGET_WGS, SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES)
+// or sqllm_test_tuning() may override them.  Every value gives the same
+// result within the stated tolerance (bit-identical while split <= 2).
 struct Tuning {
     int target_wgs = 256;   // workgroups the column split aims for (one per compute unit)
     int min_gps = 8;        // fewest column groups per workgroup (pair-table build amortisation)
     int force_split = 0;    // 0: choose; else workgroups per row tile
     int force_waves = 0;    // 0: choose; else waves per workgroup
-    int sparse_waves = 8;   // waves per workgroup of the outlier-only kernel
     Tuning()
     {
         auto get = [](const char *name, int lo, int hi, int dflt) {
@@ -62,87 +61,61 @@ size_t workspace_need(int64_t rows, int batch)
     return (size_t)tiles_of(rows) * (size_t)batch * kTileRows * 8;
 }
 
-// Waves per workgroup and compiled groups-per-wave for gps groups; false if
-// no compiled kernel fits.
-bool fit_waves(int gps, int bits, int batch, int *waves, int *gw)
-{
-    for (int g = 1; g <= 4; ++g) {
-        int w = (gps + g - 1) / g;
-        if (tuning().force_waves) {
-            w = tuning().force_waves;
-            if ((int64_t)w * g < gps) continue;
-        }
-        if (w <= max_waves(bits, batch, g)) {
-            *waves = w;
-            *gw = g;
-            return true;
-        }
-    }
-    return false;
-}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Column split and workgroup shape for the dense modes: about target_wgs
-// workgroups, at least min_gps groups each, a wave's codes in registers,
-// everything within the LDS of one compute unit.
-bool choose_dense(KernelArgs &a, int bits, int batch, bool sparse, LaunchShape &ls)
+// Column split and waves for the dense modes: about target_wgs workgroups,
+// at least min_gps groups each.  With
+// outliers x is staged in LDS when it fits beside the pair table -- for two
+// workgroups per compute unit when there are more workgroups than units.
+void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
 {
     const int64_t T = a.tiles, G = a.groups;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        s = (tuning().target_wgs + T - 1) / T;
+        s = ceil_div(tuning().target_wgs, T);
         int64_t cap = G / tuning().min_gps;
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
     }
     if (s > G) s = G;
+    if (s > kMaxSplit) s = kMaxSplit;
     if (s < 1) s = 1;
-    for (; s <= G && s <= kMaxSplit; ++s) {
-        const int gps = (int)((G + s - 1) / s);
-        const int split = (int)((G + gps - 1) / gps); // no empty splits
-        int waves = 0, gw = 0;
-        if (!fit_waves(gps, bits, batch, &waves, &gw)) continue;
-        // x staged in LDS: the workgroup's columns, or all of them when that
-        // fits and outliers need it (their columns are anywhere in the row)
-        int x_full = split == 1;
-        size_t dyn = dynamic_lds_bytes(gps, batch, waves, sparse);
-        if (sparse && split > 1) {
-            const size_t full = dynamic_lds_bytes((int)G, batch, waves, true);
-            if (kTableBytes + full <= (size_t)kLdsBudget) {
-                x_full = 1;
-                dyn = full;
-            }
+    const int gps = (int)ceil_div(G, s);
+    a.split = (int)ceil_div(G, gps); // no empty splits
+    a.gps = gps;
+    // one workgroup per compute unit: 16 waves; more workgroups than units:
+    // 8 waves, two workgroups per unit
+    const bool two_per_cu = T * a.split > tuning().target_wgs;
+    ls.waves = tuning().force_waves ? tuning().force_waves : (two_per_cu ? kDefaultWaves : kMaxWaves);
+    a.x_lds = 0;
+    ls.dyn_lds = 0;
+    if (nnz > 0) {
+        const size_t lds = kTableBytes + staged_x_bytes(a.cols, batch);
+        if (lds <= (size_t)(two_per_cu ? kLdsBudget / 2 : kLdsBudget)) {
+            a.x_lds = 1;
+            ls.dyn_lds = staged_x_bytes(a.cols, batch);
         }
-        if (kTableBytes + dyn > (size_t)kLdsBudget) continue;
-        a.split = split;
-        a.gps = gps;
-        a.gpw = (gps + waves - 1) / waves;
-        a.x_full = x_full;
-        ls.waves = waves;
-        ls.gw = gw;
-        ls.dyn_lds = dyn;
-        return true;
     }
-    return false;
 }
 
-// Outlier-only kernel: about 256 nonzeros per wave on average.
+// Outlier-only kernel: about kSparseShare nonzeros per wave; x staged in LDS
+// when it fits.
 void choose_sparse(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
 {
-    const int waves = tuning().force_waves ? tuning().force_waves : tuning().sparse_waves;
+    const int waves = tuning().force_waves ? tuning().force_waves : kDefaultWaves;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        const int64_t per_tile = (nnz + a.tiles - 1) / a.tiles;
-        s = (per_tile + waves * 256 - 1) / (waves * 256);
+        const int64_t per_tile = ceil_div(nnz, a.tiles);
+        s = ceil_div(per_tile, (int64_t)waves * kSparseShare);
     }
     if (s > kMaxSplit) s = kMaxSplit;
     if (s < 1) s = 1;
     a.split = (int)s;
     a.gps = 0;
-    a.gpw = 0;
     ls.waves = waves;
-    ls.gw = 1;
-    a.x_full = 0; // outlier gathers read x from global memory (L2)
-    ls.dyn_lds = dynamic_lds_bytes(0, batch, waves, true);
+    const size_t staged = staged_x_bytes(a.cols, batch);
+    a.x_lds = static_lds_bytes(false, batch) + staged <= (size_t)kLdsBudget;
+    ls.dyn_lds = a.x_lds ? staged : 0;
 }
 
 sqllm_status common_checks(int64_t rows, int64_t cols, const uint16_t *x, int batch, const uint16_t *y)
@@ -265,12 +238,11 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     a.row_ptr = row_ptr;
     a.col = col_idx;
     a.val = val;
-    const bool sparse = nnz > 0;
     LaunchShape ls{};
-    if (!choose_dense(a, bits, batch, sparse, ls)) return SQLLM_ERR_SHAPE;
+    choose_dense(a, batch, nnz, ls);
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
-    if (launch_dense_sparse(a, bits, batch, sparse ? kFused : kDenseOnly, ls, stream) != hipSuccess)
+    if (launch_dense_sparse(a, bits, batch, nnz > 0 ? kFused : kDenseOnly, ls, stream) != hipSuccess)
         return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }

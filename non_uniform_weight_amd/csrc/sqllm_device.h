@@ -3,31 +3,40 @@
 // §3.4 "Kernel Implementation"; storage per §3.4 "The 3/4-bit storage
 // format").  Included by the translation units that instantiate it.
 //
-// Mapping: one wave = 64 rows (one lane = one output row), so
-//   * codes stream in as 128-bit loads: the packed layout puts the same
-//     16-byte piece of 64 consecutive rows next to each other, one wave-wide
-//     load moves 1 KiB of contiguous codes; a wave issues the loads of all
-//     its column groups before it computes anything;
-//   * every lane owns its own copy of its row's lookup table in LDS, as a
-//     *pair* table: entry e holds the two centroids of code pair e as one
-//     half2 at byte (e << 8) | (lane << 2) -- a lookup is one conflict-free
-//     32-bit LDS read (the bank is the lane) feeding one v_dot2_f32_f16;
-//     one v_perm_b32 turns a packed byte into that address (4-bit: every
-//     pair is a byte; 3-bit: 12 of 16 pairs are the low six bits of a byte,
-//     the table repeats over the two ignored top bits, and the other 4 pairs
-//     are gathered from the top bits with 6 shifts/masks per 16 pairs);
-//   * all lanes of a wave work on the same columns at the same time, so the
-//     activation pairs are wave-uniform: the workgroup stages its columns of
-//     x in LDS once and every wave reads them with broadcast 128-bit reads;
-//   * a row tile's columns may be split over several workgroups; each one
-//     adds its fp32 row sums into a (sum, count) word per output with a
-//     compare-and-swap, and the one that completes the count rounds and
-//     writes y -- no fences or cache flushes, one atomic round trip;
-//   * the tile's CSR outliers are shared evenly by all waves of all its
-//     workgroups (balanced regardless of per-row skew: §3.4 "Kernel
-//     Implementation", balanced sparse kernel; Appendix C), reduced per row
-//     with a segmented scan across the wave, and summed with the dense part
-//     in fp32 before the single rounding (kernel fusion).
+// One workgroup owns one row tile (64 rows, one per lane) and a range of its
+// 256-column groups.  Its waves take one of two roles:
+//
+//   dense waves stream packed codes.  The layout puts the same 16-byte piece
+//   of 64 consecutive rows side by side, so one wave-wide 128-bit load moves
+//   1 KiB of contiguous codes.  Each wave keeps a ring of `ring_depth` groups
+//   in flight (codes plus that group's activations) and computes one group
+//   while the next ones arrive.  A lookup reads the lane's own copy of its
+//   row's *pair* table in LDS: entry e holds the two centroids of code pair e
+//   as one half2 at byte (e << 8) | (lane << 2), so a lookup is one
+//   conflict-free 32-bit LDS read (the bank is the lane), addressed by one
+//   v_perm_b32 straight from a packed byte (4-bit: every pair is a byte;
+//   3-bit: 12 of 16 pairs are the low six bits of a byte and the table repeats
+//   over the two ignored top bits, the other 4 pairs are gathered from the top
+//   bits).  The activation pairs are the same for every lane, so they stay in
+//   registers: lane n of each 16-lane row holds pairs 4n..4n+3 (and
+//   64+4n..64+4n+3) of the group, and v_dot2c_f32_f16 takes its x operand
+//   through a DPP row_newbcast:n, which hands lane n's pair to its whole row.
+//
+//   sparse waves take an even share of the tile's CSR nonzeros (balanced
+//   whatever the per-row skew: §3.4 "Kernel Implementation", balanced sparse
+//   kernel; Appendix C), 64 per lane-wide chunk, a round of chunks in flight
+//   at a time.  Each nonzero finds its row by a binary search over the
+//   tile's row pointers (held one per lane), gathers x (from LDS in the
+//   outlier-only kernel, which stages it there, else from the cache), and the
+//   products are summed per row by a segmented scan across the wave; each
+//   row's lane then fetches its sum.
+//
+// The waves' fp32 row sums are added in a fixed order; the sparse part joins
+// the dense part in fp32 before the single rounding (kernel fusion).  A row
+// tile's columns may be split over several workgroups: each adds its fp32
+// sums into a (sum, count) word per output with a compare-and-swap and the
+// one that completes the count rounds and writes y -- no fences or cache
+// flushes, one atomic round trip.
 #ifndef SQLLM_DEVICE_H
 #define SQLLM_DEVICE_H
 
@@ -43,6 +52,20 @@ namespace dev {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Zeros read by the ring's placeholder loads: a wave always issues the same
+// number of loads per step, so the compiler's wait counts stay exact; a wave
+// past its last group reads these 8 KiB (cache resident) instead of codes.
+__device__ __attribute__((aligned(16))) uint32_t g_placeholder[8 * 64 * 4];
+
+// Workgroup barrier that orders LDS accesses only: outstanding global loads
+// (the ring) stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
@@ -78,81 +101,283 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
     }
 }
 
-template <int BITS, int B, int P>
-__device__ __forceinline__ void mac_pair(const uint32_t *d, uint32_t lane4, const uint32_t *tab, const u32x4 *xq,
-                                         float *acc)
+// Registers of one group in flight: codes, and the group's activations
+// (xr[b][0..3] = pairs 4n..4n+3, xr[b][4..7] = pairs 64+4n..64+4n+3 with
+// n = lane % 16, for batch column b).
+template <int BITS, int B>
+struct GroupRegs {
+    uint32_t d[Format<BITS>::kDwords];
+    uint32_t xr[B][8];
+};
+
+// Groups a dense wave keeps in flight, sized so the ring stays within 64
+// (3-bit) or 72 (4-bit, whose table items and lookups need more) of the 128
+// registers a wave has when 16 waves share a compute unit.
+constexpr int ring_depth(int bits, int batch)
 {
-    const uint32_t a = pair_address<BITS, P>(d, lane4);
-    const half2_t w = __builtin_bit_cast(half2_t, *(const uint32_t *)((const char *)tab + a));
+    const int per = 8 * bits + 8 * batch;
+    const int d = (bits == 3 ? 80 : 72) / per;
+    return d < 1 ? 1 : (d > 3 ? 3 : d);
+}
+
+// Loads of group g of tile t into r; g < 0 loads placeholders.
+template <int BITS, int B>
+__device__ __forceinline__ void load_group(GroupRegs<BITS, B> &r, const KernelArgs &a, int t, int g, int lane)
+{
+    constexpr int NP = Format<BITS>::kPieces;
+    const bool real = g >= 0;
+    const u32x4 *src = real ? (const u32x4 *)a.packed + ((int64_t)t * a.groups + g) * NP * 64
+                            : (const u32x4 *)g_placeholder;
+    src += lane;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+        const u32x4 v = __builtin_nontemporal_load(src + q * 64);
+        r.d[4 * q + 0] = v.x;
+        r.d[4 * q + 1] = v.y;
+        r.d[4 * q + 2] = v.z;
+        r.d[4 * q + 3] = v.w;
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const uint32_t xv = xq[b][P & 3];
-        acc[b] = __builtin_amdgcn_fdot2(w, __builtin_bit_cast(half2_t, xv), acc[b], false);
+        const u32x4 *xs = real ? (const u32x4 *)((const uint32_t *)a.x + (int64_t)b * (a.cols >> 1) + g * 128)
+                               : (const u32x4 *)g_placeholder;
+        xs += lane & 15;
+        const u32x4 lo = xs[0], hi = xs[16];
+        r.xr[b][0] = lo.x;
+        r.xr[b][1] = lo.y;
+        r.xr[b][2] = lo.z;
+        r.xr[b][3] = lo.w;
+        r.xr[b][4] = hi.x;
+        r.xr[b][5] = hi.y;
+        r.xr[b][6] = hi.z;
+        r.xr[b][7] = hi.w;
     }
 }
 
-// Four pairs 4Q..4Q+3: one broadcast 128-bit LDS read of x per batch column.
+// Independent fp32 accumulators per batch column: the products of one
+// batch of pairs rotate over acc_chains(B) chains so that no v_dot2c reads an
+// accumulator the instruction before it wrote.  The chains are added in a
+// fixed order at the end.
+constexpr int acc_chains(int batch) { return batch == 1 ? 3 : (batch == 2 ? 2 : 1); }
+
+// The group's math runs in batches of 8 pairs: the table reads of batch
+// Q+1 are issued before the products of batch Q, and one wait per batch
+// (instead of one per read) covers them.
+constexpr int kBatch = 8;
+
 template <int BITS, int B, int Q>
-__device__ __forceinline__ void mac_quad(const uint32_t *d, uint32_t lane4, const uint32_t *tab, const uint32_t *xs,
-                                         int xstride, float *acc)
+__device__ __forceinline__ void batch_reads(const GroupRegs<BITS, B> &r, uint32_t lane4, const uint32_t *tab,
+                                            uint32_t (&wv)[kBatch])
 {
-    u32x4 xq[B];
+    uint32_t addr[kBatch];
+    [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+        ((addr[Ks] = pair_address<BITS, Q * kBatch + Ks>(r.d, lane4)), ...);
+    }(std::make_integer_sequence<int, kBatch>{});
 #pragma unroll
-    for (int b = 0; b < B; ++b) xq[b] = *(const u32x4 *)(xs + b * xstride + 4 * Q);
-    mac_pair<BITS, B, 4 * Q + 0>(d, lane4, tab, xq, acc);
-    mac_pair<BITS, B, 4 * Q + 1>(d, lane4, tab, xq, acc);
-    mac_pair<BITS, B, 4 * Q + 2>(d, lane4, tab, xq, acc);
-    mac_pair<BITS, B, 4 * Q + 3>(d, lane4, tab, xq, acc);
+    for (int k = 0; k < kBatch; ++k) wv[k] = *(const uint32_t *)((const char *)tab + addr[k]);
 }
 
-template <int BITS, int B, int... Qs>
-__device__ __forceinline__ void mac_group_impl(const uint32_t *d, uint32_t lane4, const uint32_t *tab,
-                                               const uint32_t *xs, int xstride, float *acc,
-                                               std::integer_sequence<int, Qs...>)
-{
-    (mac_quad<BITS, B, Qs>(d, lane4, tab, xs, xstride, acc), ...);
-}
+// The products of one batch, v_dot2c_f32_f16 with fp32 accumulation: the
+// table entry w of pair P times the activation pair P, which lane n = (P %
+// 64) / 4 of each 16-lane row holds (component P % 4 of the group's x
+// registers 4h..4h+3, h = P / 64) and a DPP row_newbcast:n operand hands to
+// the whole row.  Batch Q (pairs 8Q..8Q+7) reads x registers 4h..4h+3 with
+// h = Q / 8 through lanes n0 = 2 (Q % 8) (pairs 8Q..8Q+3) and n0 + 1.
+//
+// Two hazards need wait states the compiler cannot insert inside asm: a DPP
+// instruction must not read a register written by one of the two VALU
+// instructions before it, and a register written by a dot instruction may
+// be read by another VALU instruction only three instructions later.  The
+// products of a batch therefore form one asm block that opens with two
+// wait states and closes with three (whatever the compiler places around
+// it: it may copy accumulators between blocks), and inside it the chains
+// rotate so that each accumulator is written at least three instructions
+// before it is read again.  Activation and table registers are only ever
+// written by memory loads.
+#define SQLLM_DOT(a, x, w, n) "v_dot2c_f32_f16_dpp %[" a "], %[" x "], %[" w "] row_newbcast:%[" n "] row_mask:0xf bank_mask:0xf\n"
 
-// 128 pairs (256 codes) of one group; xs = the group's 128 x pairs (LDS),
-// batch column b at xs + b * xstride.
-template <int BITS, int B>
-__device__ __forceinline__ void mac_group(const uint32_t *d, uint32_t lane4, const uint32_t *tab, const uint32_t *xs,
-                                          int xstride, float *acc)
-{
-    mac_group_impl<BITS, B>(d, lane4, tab, xs, xstride, acc, std::make_integer_sequence<int, 32>{});
-}
+template <int B, int N0>
+struct BatchDots;
 
-template <int BITS>
-__device__ __forceinline__ void load_group(const u32x4 *__restrict__ src, uint32_t *d)
-{
-#pragma unroll
-    for (int q = 0; q < Format<BITS>::kPieces; ++q) {
-        const u32x4 v = __builtin_nontemporal_load(src + q * 64);
-        d[4 * q + 0] = v.x;
-        d[4 * q + 1] = v.y;
-        d[4 * q + 2] = v.z;
-        d[4 * q + 3] = v.w;
+template <int N0>
+struct BatchDots<1, N0> { // chains k % 3
+    static __device__ __forceinline__ void run(const uint32_t *x, const uint32_t *w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOT("a0", "x0", "w0", "n0") SQLLM_DOT("a1", "x1", "w1", "n0")
+                         SQLLM_DOT("a2", "x2", "w2", "n0") SQLLM_DOT("a0", "x3", "w3", "n0")
+                             SQLLM_DOT("a1", "x0", "w4", "n1") SQLLM_DOT("a2", "x1", "w5", "n1")
+                                 SQLLM_DOT("a0", "x2", "w6", "n1") SQLLM_DOT("a1", "x3", "w7", "n1") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [w0] "v"(w[0]),
+                       [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [w4] "v"(w[4]), [w5] "v"(w[5]),
+                       [w6] "v"(w[6]), [w7] "v"(w[7]), [n0] "n"(N0), [n1] "n"(N0 + 1));
     }
+};
+
+template <int N0>
+struct BatchDots<2, N0> { // acc[b * 2 + k % 2]; x[b * 4 + c]
+    static __device__ __forceinline__ void run(const uint32_t *x, const uint32_t *w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOT("a00", "x00", "w0", "n0") SQLLM_DOT("a10", "x10", "w0", "n0")
+                         SQLLM_DOT("a01", "x01", "w1", "n0") SQLLM_DOT("a11", "x11", "w1", "n0")
+                             SQLLM_DOT("a00", "x02", "w2", "n0") SQLLM_DOT("a10", "x12", "w2", "n0")
+                                 SQLLM_DOT("a01", "x03", "w3", "n0") SQLLM_DOT("a11", "x13", "w3", "n0")
+                                     SQLLM_DOT("a00", "x00", "w4", "n1") SQLLM_DOT("a10", "x10", "w4", "n1")
+                                         SQLLM_DOT("a01", "x01", "w5", "n1") SQLLM_DOT("a11", "x11", "w5", "n1")
+                                             SQLLM_DOT("a00", "x02", "w6", "n1") SQLLM_DOT("a10", "x12", "w6", "n1")
+                                                 SQLLM_DOT("a01", "x03", "w7", "n1")
+                                                     SQLLM_DOT("a11", "x13", "w7", "n1") "s_nop 2\n"
+                     : [a00] "+v"(acc[0]), [a01] "+v"(acc[1]), [a10] "+v"(acc[2]), [a11] "+v"(acc[3])
+                     : [x00] "v"(x[0]), [x01] "v"(x[1]), [x02] "v"(x[2]), [x03] "v"(x[3]), [x10] "v"(x[4]),
+                       [x11] "v"(x[5]), [x12] "v"(x[6]), [x13] "v"(x[7]), [w0] "v"(w[0]), [w1] "v"(w[1]),
+                       [w2] "v"(w[2]), [w3] "v"(w[3]), [w4] "v"(w[4]), [w5] "v"(w[5]), [w6] "v"(w[6]),
+                       [w7] "v"(w[7]), [n0] "n"(N0), [n1] "n"(N0 + 1));
+    }
+};
+
+// Batch columns 3 and up: one chain each; a block per pair (the columns'
+// products are B >= 3 instructions apart).
+#define SQLLM_DOTS3(n) SQLLM_DOT("a0", "x0", "w", n) SQLLM_DOT("a1", "x1", "w", n) SQLLM_DOT("a2", "x2", "w", n)
+#define SQLLM_PAIR_OPERANDS(w_)                                                                                    \
+    [w] "v"(w_), [n] "n"(N)
+
+template <int B, int N>
+struct PairDots;
+
+template <int N>
+struct PairDots<3, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), SQLLM_PAIR_OPERANDS(w));
+    }
+};
+template <int N>
+struct PairDots<4, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") SQLLM_DOT("a3", "x3", "w", "n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), SQLLM_PAIR_OPERANDS(w));
+    }
+};
+template <int N>
+struct PairDots<5, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") SQLLM_DOT("a3", "x3", "w", "n") SQLLM_DOT("a4", "x4", "w", "n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]),
+                       [a4] "+v"(acc[4])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [x4] "v"(x[4]),
+                       SQLLM_PAIR_OPERANDS(w));
+    }
+};
+template <int N>
+struct PairDots<6, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") SQLLM_DOT("a3", "x3", "w", "n") SQLLM_DOT("a4", "x4", "w", "n")
+                         SQLLM_DOT("a5", "x5", "w", "n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]),
+                       [a4] "+v"(acc[4]), [a5] "+v"(acc[5])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [x4] "v"(x[4]),
+                       [x5] "v"(x[5]), SQLLM_PAIR_OPERANDS(w));
+    }
+};
+template <int N>
+struct PairDots<7, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") SQLLM_DOT("a3", "x3", "w", "n") SQLLM_DOT("a4", "x4", "w", "n")
+                         SQLLM_DOT("a5", "x5", "w", "n") SQLLM_DOT("a6", "x6", "w", "n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]),
+                       [a4] "+v"(acc[4]), [a5] "+v"(acc[5]), [a6] "+v"(acc[6])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [x4] "v"(x[4]),
+                       [x5] "v"(x[5]), [x6] "v"(x[6]), SQLLM_PAIR_OPERANDS(w));
+    }
+};
+template <int N>
+struct PairDots<8, N> {
+    static __device__ __forceinline__ void run(const uint32_t *x, uint32_t w, float *acc)
+    {
+        asm volatile("s_nop 1\n" SQLLM_DOTS3("n") SQLLM_DOT("a3", "x3", "w", "n") SQLLM_DOT("a4", "x4", "w", "n")
+                         SQLLM_DOT("a5", "x5", "w", "n") SQLLM_DOT("a6", "x6", "w", "n")
+                             SQLLM_DOT("a7", "x7", "w", "n") "s_nop 2\n"
+                     : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]),
+                       [a4] "+v"(acc[4]), [a5] "+v"(acc[5]), [a6] "+v"(acc[6]), [a7] "+v"(acc[7])
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [x4] "v"(x[4]),
+                       [x5] "v"(x[5]), [x6] "v"(x[6]), [x7] "v"(x[7]), SQLLM_PAIR_OPERANDS(w));
+    }
+};
+
+// acc[b * acc_chains(B) + chain]
+template <int BITS, int B, int Q>
+__device__ __forceinline__ void batch_macs(const GroupRegs<BITS, B> &r, const uint32_t (&wv)[kBatch], float *acc)
+{
+    constexpr int h = Q / 8, n0 = 2 * (Q % 8);
+    if constexpr (B <= 2) {
+        uint32_t x[4 * B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[4 * b + c] = r.xr[b][4 * h + c];
+        BatchDots<B, n0>::run(x, wv, acc);
+    } else {
+        [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+            (
+                [&] {
+                    uint32_t x[B];
+#pragma unroll
+                    for (int b = 0; b < B; ++b) x[b] = r.xr[b][4 * h + Ks % 4];
+                    PairDots<B, n0 + Ks / 4>::run(x, wv[Ks], acc);
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, kBatch>{});
+    }
+}
+
+// All 128 pairs (256 codes) of one group.
+template <int BITS, int B>
+__device__ __forceinline__ void mac_group(const GroupRegs<BITS, B> &r, uint32_t lane4, const uint32_t *tab,
+                                          float *acc)
+{
+    constexpr int NQ = 128 / kBatch;
+    uint32_t wv[2][kBatch];
+    batch_reads<BITS, B, 0>(r, lane4, tab, wv[0]);
+    [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
+        (
+            [&] {
+                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
+                // one wait for the whole batch: the empty statement needs all
+                // eight table reads of batch Qs
+                const uint32_t(&cur)[kBatch] = wv[Qs & 1];
+                asm volatile("" ::"v"(cur[0]), "v"(cur[1]), "v"(cur[2]), "v"(cur[3]), "v"(cur[4]), "v"(cur[5]),
+                             "v"(cur[6]), "v"(cur[7]));
+                batch_macs<BITS, B, Qs>(r, cur, acc);
+            }(),
+            ...);
+    }(std::make_integer_sequence<int, NQ>{});
 }
 
 // Pair table of the tile (256 entries per lane).  Work item (lane l, low
 // code h): lo = LUT[row][h]; for every high code c, entry h | c << b (3-bit:
 // also with both ignored top bits set every way) = lo | LUT[row][c] << 16.
-// An item's loads (the row's table and lo) are issued apart from its stores
-// so that they can go out ahead of the bulk code loads.
-template <int BITS>
-struct TableItem {
+// A thread's items idx = threadIdx.x + k * blockDim.x (k < N) all belong to
+// lane idx % 64, so they share one load of the row's table.  The loads are
+// issued apart from the stores so that they go out ahead of the code loads.
+template <int BITS, int N>
+struct TableItems {
     uint32_t lw[Format<BITS>::kEntries / 2];
-    uint32_t lo;
+    uint32_t lo[N];
 };
 
-template <int BITS>
-__device__ __forceinline__ void table_item_load(TableItem<BITS> &it, const uint16_t *__restrict__ lut, int idx,
-                                                int row0, int rows)
+template <int BITS, int N>
+__device__ __forceinline__ void table_items_load(TableItems<BITS, N> &it, const uint16_t *__restrict__ lut,
+                                                 int idx0, int stride, int row0, int rows)
 {
     constexpr int E = Format<BITS>::kEntries;
-    const int l = idx & 63, h = idx >> 6;
-    const int r = min(row0 + l, rows - 1);
+    const int r = min(row0 + (idx0 & 63), rows - 1);
     const u32x4 *lrow = (const u32x4 *)(lut + (int64_t)r * E);
 #pragma unroll
     for (int q = 0; q < E / 8; ++q) {
@@ -162,102 +387,156 @@ __device__ __forceinline__ void table_item_load(TableItem<BITS> &it, const uint1
         it.lw[4 * q + 2] = v.z;
         it.lw[4 * q + 3] = v.w;
     }
-    it.lo = lut[(int64_t)r * E + h];
+#pragma unroll
+    for (int k = 0; k < N; ++k) { // items past the table load a valid entry and are not stored
+        const int h = min((idx0 + k * stride) >> 6, E - 1);
+        it.lo[k] = lut[(int64_t)r * E + h];
+    }
 }
 
-template <int BITS>
-__device__ __forceinline__ void table_item_store(const TableItem<BITS> &it, uint32_t *tab, int idx)
+template <int BITS, int N>
+__device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it, uint32_t *tab, int idx0, int stride)
 {
     constexpr int E = Format<BITS>::kEntries;
-    const int l = idx & 63, h = idx >> 6;
+    const int l = idx0 & 63;
 #pragma unroll
-    for (int c = 0; c < E; ++c) {
-        const uint32_t hi = (c & 1) ? (it.lw[c >> 1] & 0xFFFF0000u) : (it.lw[c >> 1] << 16);
-        const uint32_t v = it.lo | hi;
-        if constexpr (BITS == 4) {
-            tab[(h | (c << 4)) * 64 + l] = v;
-        } else {
+    for (int k = 0; k < N; ++k) {
+        const int h = (idx0 + k * stride) >> 6;
+        if (h >= E) break;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tab[(h | (c << 3) | (j << 6)) * 64 + l] = v;
-        }
-    }
-}
-
-// Row (0..63) of nonzero i of the tile: largest r with rps[r] <= i.
-__device__ __forceinline__ int tile_row_of(const int *rps, int i)
-{
-    int lo = 0;
+        for (int c = 0; c < E; ++c) {
+            const uint32_t hi = (c & 1) ? (it.lw[c >> 1] & 0xFFFF0000u) : (it.lw[c >> 1] << 16);
+            const uint32_t v = it.lo[k] | hi;
+            if constexpr (BITS == 4) {
+                tab[(h | (c << 4)) * 64 + l] = v;
+            } else {
 #pragma unroll
-    for (int step = 32; step >= 1; step >>= 1)
-        if (rps[lo + step] <= i) lo += step;
-    return lo;
-}
-
-// A batch of up to kSparseBatch chunks of 64 nonzeros: column, value, row.
-struct SparseBatch {
-    int col[kSparseBatch];
-    int row[kSparseBatch];
-    float val[kSparseBatch];
-};
-
-// Loads of nonzeros [base, base + kSparseBatch*64) clipped to v1.
-__device__ __forceinline__ void sparse_batch_load(SparseBatch &sb, const KernelArgs &a, int base, int v1, int lane)
-{
-#pragma unroll
-    for (int k = 0; k < kSparseBatch; ++k) {
-        const int i = base + k * 64 + lane;
-        sb.col[k] = 0;
-        sb.val[k] = 0.f;
-        if (i < v1) {
-            sb.col[k] = a.col[i];
-            sb.val[k] = f16_to_f32(a.val[i]);
-        }
-    }
-}
-
-// Row (0..63) of each nonzero of the batch, products with x, summed per row
-// (segmented scan over the wave: rows are non-decreasing along the CSR) into
-// the wave's LDS row sums rsum[b * 64 + r].  x from LDS (xh, all columns,
-// batch column b at xh + b * xhs) when staged there, else from global memory.
-template <int B>
-__device__ __forceinline__ void sparse_batch_finish(const SparseBatch &sb, const KernelArgs &a, const int *rps,
-                                                    const uint16_t *xh, int xhs, int base, int v1, int lane,
-                                                    float *rsum)
-{
-    float xv[kSparseBatch][B];
-    int row[kSparseBatch];
-#pragma unroll
-    for (int k = 0; k < kSparseBatch; ++k) {
-        const int i = base + k * 64 + lane;
-        row[k] = i < v1 ? tile_row_of(rps, i) : 64; // 64: never a real row
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            xv[k][b] = f16_to_f32(xh ? xh[b * xhs + sb.col[k]] : a.x[(int64_t)b * a.cols + sb.col[k]]);
-    }
-#pragma unroll
-    for (int k = 0; k < kSparseBatch; ++k) {
-        if (base + k * 64 >= v1) break;
-        float prod[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) prod[b] = sb.val[k] * xv[k][b];
-        const int r = row[k];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int ru = __shfl_up(r, off, 64);
-            const bool same = lane >= off && ru == r;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float pu = __shfl_up(prod[b], off, 64);
-                if (same) prod[b] += pu;
+                for (int j = 0; j < 4; ++j) tab[(h | (c << 3) | (j << 6)) * 64 + l] = v;
             }
         }
-        const int rn = __shfl_down(r, 1, 64);
-        if (r < 64 && (lane == 63 || rn != r)) {
-#pragma unroll
-            for (int b = 0; b < B; ++b) rsum[b * 64 + r] += prod[b];
-        }
     }
 }
+
+// Chunks of 64 nonzeros a wave loads per round: column | fp16 value << 16,
+// one register per chunk, held through the dense steps (fewer where the
+// ring is large).
+constexpr int round_chunks(int bits, int batch) { return bits == 3 && batch == 1 ? 8 : 4; }
+
+// Loads of nonzeros [base, base + 64 * R): column and raw fp16 value of one
+// nonzero per lane and chunk, each zero-extended in a register of its own (so
+// that nothing waits for them before they are used).  Lanes past v1 load
+// nonzero v1 - 1 (any valid index would do; their products are dropped), so
+// a round always issues the same number of loads and the waits stay exact.
+template <int R>
+struct SparseRound {
+    uint32_t col[R];
+    uint32_t val[R];
+};
+
+template <int R>
+__device__ __forceinline__ void sparse_round_load(SparseRound<R> &sr, const KernelArgs &a, int base, int v1, int lane)
+{
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int ic = max(min(base + k * 64 + lane, v1 - 1), 0);
+        sr.col[k] = a.col[ic];
+        sr.val[k] = a.val[ic];
+    }
+}
+
+__device__ __forceinline__ int lane_read(int src_lane, int v) { return __builtin_amdgcn_ds_bpermute(src_lane << 2, v); }
+__device__ __forceinline__ float lane_read(int src_lane, float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+// Value of v from lane p - N of the same 16-lane row (0 for the row's first
+// N lanes), and the last value of the previous row(s) (row_bcast: lane 15 of
+// each row to rows 1 and 3, lane 31 to rows 2 and 3; 0 elsewhere).
+template <int N>
+__device__ __forceinline__ float row_shr(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_bcast15(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+}
+__device__ __forceinline__ float row_bcast31(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+}
+
+// Adds S x of the chunk of nonzeros [cb, min(cb + 64, v1)) (this lane's:
+// column colv, fp16 value valv; lanes past v1 contribute nothing) into the
+// row lanes' acc.  rp_lo / rp_hi: row pointers of this lane's row and the
+// next one (lane = row of the tile).  x from LDS (XL: staged [B][cols] fp16
+// at xl) or global memory.  acc[b * NC] is batch column b's first chain.
+//
+// The chunk's rows are non-decreasing, so their products form contiguous
+// segments.  Each row that starts inside the chunk marks its first lane
+// (a forward lane permute), a ballot turns the marks into a wave-wide mask,
+// and every lane's segment start is the mask's highest bit at or below it.
+// A segmented inclusive scan (DPP row shifts, then row broadcasts) sums each
+// segment up to every lane, and each row lane fetches the value at its last
+// nonzero in the chunk.
+template <int B, int NC, bool XL>
+__device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int cb, int v1, const KernelArgs &a, int lane,
+                                             int rp_lo, int rp_hi, const uint16_t *xl, float *acc)
+{
+    const int i = cb + lane;
+    const int s_r = rp_lo - cb; // chunk lane of this row's first nonzero
+    const bool starts = rp_lo < rp_hi && s_r > 0 && s_r < 64;
+    const int mark = __builtin_amdgcn_ds_permute((starts ? s_r : 0) << 2, 1); // rows without a start mark lane 0
+    const uint64_t starts_mask = __builtin_amdgcn_ballot_w64(mark != 0) | 1ull;
+    const uint64_t upto = starts_mask & (~0ull >> (63 - lane));
+    const int seg0 = 63 - (int)__builtin_clzll(upto); // first lane of this nonzero's segment
+    const float vv = i < v1 ? f16_to_f32((uint16_t)valv) : 0.f;
+    const int col = (int)colv;
+    float prod[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const int64_t xi = (int64_t)b * a.cols + col;
+        prod[b] = vv * f16_to_f32(XL ? xl[xi] : a.x[xi]);
+    }
+    const int row_first = lane & ~15;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float v = prod[b];
+        float u = row_shr<1>(v);
+        if (lane - 1 >= seg0) v += u;
+        u = row_shr<2>(v);
+        if (lane - 2 >= seg0) v += u;
+        u = row_shr<4>(v);
+        if (lane - 4 >= seg0) v += u;
+        u = row_shr<8>(v);
+        if (lane - 8 >= seg0) v += u;
+        u = row_bcast15(v);
+        if (seg0 < row_first) v += u; // rows 1 and 3 (u is 0 in rows 0 and 2)
+        u = row_bcast31(v);
+        if (seg0 < 32) v += u; // rows 2 and 3 (u is 0 in rows 0 and 1)
+        prod[b] = v;
+    }
+    // lane r: the sum of row r's nonzeros in this chunk sits at the chunk lane
+    // of its last one
+    const int hi = min(min(rp_hi, cb + 64), v1);
+    const bool present = max(rp_lo, cb) < hi;
+    const int e = present ? hi - 1 - cb : 0;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float got = lane_read(e, prod[b]);
+        if (present) acc[b * NC] += got;
+    }
+}
+
+// Issue the first ring of code loads only after the pair table is built:
+// behind a deep queue of streaming code loads the table's own loads return
+// late and hold back every group's math.
+constexpr bool kRingAfterTable = true;
+
+// Quads (16 bytes) of x each thread stages in LDS from registers loaded in
+// the prologue; wider x is copied after the ring is issued.
+constexpr int kStageQuads = 4;
 
 // Round and store (or hand over) this workgroup's fp32 row sums.
 template <int B, bool ADDY>
@@ -303,218 +582,257 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
 
 // ---------------------------------------------------------------------------
 // The kernel.  MODE: kFused y = (D+S)x; kDenseOnly y = Dx; kSparseAdd y += Sx.
-// Grid: tiles * split workgroups, workgroup (tile t, split s) owns column
-// groups [s*gps, min((s+1)*gps, groups)); wave w of it owns gpw <= GW of
-// them.  Dynamic LDS: x [B][xstride pairs] -- every column when a.x_full,
-// else only the workgroup's -- then (outlier modes) 65 row pointers and
-// [waves][B][64] fp32 row sums.
+// Grid: tiles * split workgroups; workgroup (tile t, split s) owns column
+// groups [s*gps, min((s+1)*gps, groups)) and share s of the tile's nonzeros.
+// Every wave does both kinds of work: dense groups gb + w + j*W, and one of
+// the split * W even shares of the tile's nonzeros, a chunk after each dense
+// group (the rest after the last one).
+// LDS: the pair table (static, dense modes; it must stay the only static
+// array so that it starts at LDS address 0) and, when a.x_lds, all of x for
+// the outlier gathers (dynamic, [B][cols] fp16).
 //
-// Order of work: the small loads (x, the pair-table rows, row pointers) go
-// out first, the codes right behind them; the table is built while the
-// codes stream in; outlier loads are issued before the dense work and used
-// after it.
-// Register room: with 16 waves per workgroup (128 VGPRs each) a wave holds
-// its codes plus ~8 registers per batch column only up to 96 dwords; beyond
-// that the kernel is compiled for at most 8 waves.
-template <int BITS, int B, int GW>
-constexpr int max_threads() { return max_waves(BITS, B, GW) * 64; }
-
-template <int BITS, int B, int MODE, int GW>
-__global__ void __launch_bounds__((max_threads<BITS, B, GW>())) dense_sparse_kernel(KernelArgs a)
+// Order of work: row pointers, table rows and x to stage go out first, then
+// the first ring of code loads, then the first round of nonzeros.  Every dense step issues one group of loads
+// (placeholders past the wave's last group), so the wait before each group's
+// math lets exactly D-1 groups stay in flight.
+template <int BITS, int B, int MODE>
+__global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs a)
 {
     constexpr bool DENSE = MODE != kSparseAdd;
     constexpr bool SPARSE = MODE != kDenseOnly;
     constexpr bool ADDY = MODE == kSparseAdd;
-    constexpr int ND = Format<BITS>::kDwords;
     constexpr int E = Format<BITS>::kEntries;
+    constexpr int D = ring_depth(BITS, B);
+    constexpr int ITEMS = DENSE ? (64 * E) / 512 : 1; // table items per thread with 8 waves
     __shared__ __align__(16) uint32_t tab[DENSE ? kTableBytes / 4 : kMaxWaves * B * 64];
     extern __shared__ __align__(16) uint32_t dyn[];
 
     const int nt = blockDim.x;
-    const int nw = nt >> 6;
+    const int W = nt >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x / a.split, s = blockIdx.x - t * a.split;
     const int row0 = t * 64;
     const uint32_t lane4 = (uint32_t)lane << 2;
+
+    constexpr int NC = acc_chains(B);
+    float acc[B * NC]; // dense chains; outliers add into chain 0
+#pragma unroll
+    for (int k = 0; k < B * NC; ++k) acc[k] = 0.f;
+
+    // -- 1. the pair-table items beyond ITEMS per thread (workgroups of fewer
+    //       than 8 waves only)
+    if constexpr (DENSE) {
+        for (int idx = threadIdx.x + ITEMS * nt; idx < 64 * E; idx += nt) {
+            TableItems<BITS, 1> it2;
+            table_items_load<BITS, 1>(it2, a.lut, idx, nt, row0, a.rows);
+            table_items_store<BITS, 1>(it2, tab, idx, nt);
+        }
+    }
+
+    // -- 2. small loads first: the tile's row pointers, this thread's table
+    //       items and quads of x to stage
+    int rp_lo = 0, rp_hi = 0;
+    if constexpr (SPARSE) {
+        rp_lo = a.row_ptr[min(row0 + lane, a.rows)];
+        rp_hi = a.row_ptr[min(row0 + lane + 1, a.rows)];
+    }
+    TableItems<BITS, ITEMS> items; // loaded by every thread (no branch), stored by those that own items
+    if constexpr (DENSE) table_items_load<BITS, ITEMS>(items, a.lut, threadIdx.x, nt, row0, a.rows);
+    const int nxq = (SPARSE && a.x_lds) ? B * (a.cols >> 3) : 0; // 16-byte quads of x to stage
+    u32x4 xq[SPARSE ? kStageQuads : 1];
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int k = 0; k < kStageQuads; ++k) // past the end: a valid quad, not stored
+            xq[k] = ((const u32x4 *)a.x)[min((int)threadIdx.x + k * nt, max(nxq - 1, 0))];
+    }
+
+    // -- 3. the first ring of code loads (here, or once the table is built:
+    //       a queue of streaming code loads delays the table's loads)
     const int gb = s * a.gps;
     const int ge = min(gb + a.gps, a.groups);
-    // staged x: pairs [xg0*128, xg1*128) of every batch column
-    const int xg0 = a.x_full ? 0 : gb, xg1 = a.x_full ? a.groups : ge;
-    const int xstride = (a.x_full ? a.groups : a.gps) * 128;
-    uint32_t *xs = dyn;
-    int *rps = (int *)(dyn + ((DENSE || a.x_full) ? B * xstride : 0));
-    float *rsum = (float *)(rps + 68) + w * B * 64;
-
-    float acc[B];
+    const int cnt = DENSE ? max(0, (ge - gb - w + W - 1) / W) : 0; // this wave's groups
+    GroupRegs<BITS, B> ring[DENSE ? D : 1];
+    auto issue_ring = [&]() {
+        if constexpr (DENSE) {
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+            for (int k = 0; k < D; ++k) load_group<BITS, B>(ring[k], a, t, k < cnt ? gb + w + k * W : -1, lane);
+        }
+    };
+    if constexpr (!kRingAfterTable) issue_ring();
 
-    // -- 1. small loads first: one x quad per batch column, one table item
-    //       and one row pointer per thread (the rest, if any, after the codes)
-    const int nq = (DENSE || a.x_full) ? (xg1 - xg0) * 32 : 0;
-    u32x4 xq[B];
-    if (threadIdx.x < nq) {
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            xq[b] = *((const u32x4 *)(a.x + (int64_t)b * a.cols + (int64_t)xg0 * 256) + threadIdx.x);
-    }
-    TableItem<BITS> item;
-    if constexpr (DENSE) {
-        if (threadIdx.x < 64 * E) table_item_load<BITS>(item, a.lut, threadIdx.x, row0, a.rows);
-    }
-    // row pointers of the tile: rps[0..63] by the first wave, rps[64] (the
-    // tile's end) by thread 0 too, so any block size loads all 65
-    int rpv = 0, rpv_end = 0;
+    // -- 4. this wave's share of the nonzeros and its first round of loads
+    int nz0 = 0, v0 = 0, v1 = 0;
+    constexpr int R = round_chunks(BITS, B);
+    SparseRound<R> cv;
     if constexpr (SPARSE) {
-        if (threadIdx.x < 64) rpv = a.row_ptr[min(row0 + (int)threadIdx.x, a.rows)];
-        if (threadIdx.x == 0) rpv_end = a.row_ptr[min(row0 + 64, a.rows)];
+        // the tile's ends, as uniform (scalar) loads: waiting for them does
+        // not wait for the vector loads in flight
+        typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr; // read-only: scalar loads
+        const const_i32_ptr rptr = (const_i32_ptr)a.row_ptr;
+        nz0 = rptr[row0];
+        const int nz1 = rptr[min(row0 + 64, a.rows)];
+        // share part of `parts` even shares: the first len % parts get one more
+        const uint32_t len = (uint32_t)(nz1 - nz0);
+        const uint32_t parts = (uint32_t)(a.split * W), part = (uint32_t)(w * a.split + s);
+        const uint32_t per = len / parts, extra = len - per * parts;
+        v0 = nz0 + (int)(part * per + min(part, extra));
+        v1 = v0 + (int)(per + (part < extra ? 1u : 0u));
+        sparse_round_load(cv, a, v0, v1, lane);
     }
 
-    // -- 2. every code load of this wave
-    uint32_t buf[GW][ND];
-    int ng = 0;
+    // -- 5. store the pair table and the staged x, then a barrier that
+    //       orders LDS only: the ring stays in flight across it
     if constexpr (DENSE) {
-        const int g0 = gb + w * a.gpw;
-        ng = max(0, min(a.gpw, ge - g0));
-        const u32x4 *wave_codes =
-            (const u32x4 *)a.packed + ((int64_t)t * a.groups + g0) * Format<BITS>::kPieces * 64 + lane;
+        if ((int)threadIdx.x < 64 * E) table_items_store<BITS, ITEMS>(items, tab, threadIdx.x, nt);
+    }
+    if constexpr (SPARSE) {
 #pragma unroll
-        for (int j = 0; j < GW; ++j)
-            if (j < ng) load_group<BITS>(wave_codes + j * Format<BITS>::kPieces * 64, buf[j]);
+        for (int k = 0; k < kStageQuads; ++k)
+            if ((int)threadIdx.x + k * nt < nxq) ((u32x4 *)dyn)[threadIdx.x + k * nt] = xq[k];
+        for (int i = threadIdx.x + kStageQuads * nt; i < nxq; i += nt) ((u32x4 *)dyn)[i] = ((const u32x4 *)a.x)[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (kRingAfterTable) issue_ring();
+
+    // -- 6. dense steps: a main loop in which every step refills the ring,
+    //       then the last (fewer than 2D) groups, each of those followed by
+    //       one chunk of the first round of nonzeros
+    const uint16_t *xl = (const uint16_t *)dyn;
+    const int r0end = min(v1, v0 + 64 * R);
+    auto chunk = [&](auto kc) { // chunk K of the first round, if the share has it
+        constexpr int K = decltype(kc)::value;
+        if constexpr (SPARSE && K < R) {
+            const int cbk = v0 + 64 * K;
+            if (cbk < r0end) {
+                if (a.x_lds)
+                    sparse_chunk<B, NC, true>(cv.col[K], cv.val[K], cbk, v1, a, lane, rp_lo, rp_hi, xl, acc);
+                else
+                    sparse_chunk<B, NC, false>(cv.col[K], cv.val[K], cbk, v1, a, lane, rp_lo, rp_hi, xl, acc);
+            }
+        }
+    };
+    int done = 0; // chunks of the first round taken
+    if constexpr (DENSE) {
+        int j0 = 0;
+        for (; j0 + 2 * D <= cnt; j0 += D) {
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                mac_group<BITS, B>(ring[k], lane4, tab, acc);
+                load_group<BITS, B>(ring[k], a, t, gb + w + (j0 + k + D) * W, lane);
+            }
+        }
+        [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+            (
+                [&] {
+                    constexpr int k = Ks;
+                    const int j = j0 + k;
+                    if (j < cnt) {
+                        mac_group<BITS, B>(ring[k], lane4, tab, acc);
+                        if (j + D < cnt) load_group<BITS, B>(ring[k], a, t, gb + w + (j + D) * W, lane);
+                        if (a.x_lds) {
+                            chunk(std::integral_constant<int, k>{});
+                            done = k + 1;
+                        }
+                    }
+                }(),
+                ...);
+            (
+                [&] {
+                    constexpr int k = Ks;
+                    if (j0 + D + k < cnt) {
+                        mac_group<BITS, B>(ring[k], lane4, tab, acc);
+                        if (a.x_lds) {
+                            chunk(std::integral_constant<int, D + k>{});
+                            done = D + k + 1;
+                        }
+                    }
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, D>{});
     }
 
-    // -- 3. fill LDS: x, pair table, row pointers, zeroed row sums
-    if (threadIdx.x < nq) {
+    // -- 7. the rest of the nonzeros
+    if constexpr (SPARSE) {
+        [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+            ((Ks >= done ? chunk(std::integral_constant<int, Ks>{}) : void()), ...);
+        }(std::make_integer_sequence<int, R>{});
+        for (int base = v0 + 64 * R; base < v1; base += 64 * R) {
+            sparse_round_load(cv, a, base, v1, lane);
 #pragma unroll
-        for (int b = 0; b < B; ++b) ((u32x4 *)(xs + b * xstride))[threadIdx.x] = xq[b];
-    }
-    for (int i = threadIdx.x + nt; i < nq; i += nt) {
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            ((u32x4 *)(xs + b * xstride))[i] = *((const u32x4 *)(a.x + (int64_t)b * a.cols + (int64_t)xg0 * 256) + i);
-    }
-    if constexpr (DENSE) {
-        if (threadIdx.x < 64 * E) table_item_store<BITS>(item, tab, threadIdx.x);
-        for (int idx = threadIdx.x + nt; idx < 64 * E; idx += nt) {
-            TableItem<BITS> it2;
-            table_item_load<BITS>(it2, a.lut, idx, row0, a.rows);
-            table_item_store<BITS>(it2, tab, idx);
+            for (int k = 0; k < R; ++k) {
+                if (base + 64 * k >= v1) break;
+                if (a.x_lds)
+                    sparse_chunk<B, NC, true>(cv.col[k], cv.val[k], base + 64 * k, v1, a, lane, rp_lo, rp_hi, xl,
+                                              acc);
+                else
+                    sparse_chunk<B, NC, false>(cv.col[k], cv.val[k], base + 64 * k, v1, a, lane, rp_lo, rp_hi, xl,
+                                               acc);
+            }
         }
     }
-    if constexpr (SPARSE) {
-        if (threadIdx.x < 64) rps[threadIdx.x] = rpv;
-        if (threadIdx.x == 0) rps[64] = rpv_end;
-#pragma unroll
-        for (int b = 0; b < B; ++b) rsum[b * 64 + lane] = 0.f;
-    }
-    __syncthreads();
+    lds_barrier(); // pair table no longer needed
 
-    // -- 4. outliers: the tile's nonzeros cut into shares of about 256, dealt
-    //       round-robin over the tile's workgroups, one share per wave at most;
-    //       the first batch's loads go out before the dense work
-    int v0 = 0, v1 = 0;
-    SparseBatch sb;
-    if constexpr (SPARSE) {
-        const int nz0 = rps[0];
-        const int64_t len = rps[64] - nz0;
-        int64_t parts = (int64_t)a.split * nw;
-        const int64_t want = (len + 255) / 256;
-        if (want < parts) parts = want > 0 ? want : 1;
-        const int64_t part = (int64_t)w * a.split + s;
-        if (part < parts) {
-            v0 = nz0 + (int)(len * part / parts);
-            v1 = nz0 + (int)(len * (part + 1) / parts);
-        }
-        if (v0 < v1) sparse_batch_load(sb, a, v0, v1, lane);
-    }
-
-    // -- 5. dense: look up and multiply every loaded group
-    if constexpr (DENSE) {
-        const int g0 = gb + w * a.gpw;
-#pragma unroll
-        for (int j = 0; j < GW; ++j)
-            if (j < ng) mac_group<BITS, B>(buf[j], lane4, tab, xs + (g0 + j - xg0) * 128, xstride, acc);
-    }
-
-    // -- 6. outliers: finish the first batch, then any further ones
-    if constexpr (SPARSE) {
-        const uint16_t *xh = a.x_full ? (const uint16_t *)xs : nullptr;
-        const int xhs = 2 * xstride;
-        if (v0 < v1) sparse_batch_finish<B>(sb, a, rps, xh, xhs, v0, v1, lane, rsum);
-        for (int base = v0 + kSparseBatch * 64; base < v1; base += kSparseBatch * 64) {
-            sparse_batch_load(sb, a, base, v1, lane);
-            sparse_batch_finish<B>(sb, a, rps, xh, xhs, base, v1, lane, rsum);
-        }
-    }
-    __syncthreads(); // pair table and x no longer needed
-
-    // -- 7. reduce the waves (fixed order), then round and store / hand over
+    // -- 8. reduce the waves (fixed order), then round and store / hand over
     float *red = (float *)tab;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        float v = acc[b];
-        if constexpr (SPARSE) v += rsum[b * 64 + lane];
+        float v = acc[b * NC];
+#pragma unroll
+        for (int c = 1; c < NC; ++c) v += acc[b * NC + c];
         red[(w * B + b) * 64 + lane] = v;
     }
-    __syncthreads();
+    lds_barrier();
     if (w != 0) return;
     float tot[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         float v = 0.f;
-        for (int k = 0; k < nw; ++k) v += red[(k * B + b) * 64 + lane];
+        for (int k = 0; k < W; ++k) v += red[(k * B + b) * 64 + lane];
         tot[b] = v;
     }
     finish_rows<B, ADDY>(a, t, lane, tot);
 }
 
-template <int BITS, int B, int MODE, int GW>
+template <int BITS, int B, int MODE>
 hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
-    auto kern = dense_sparse_kernel<BITS, B, MODE, GW>;
+    auto kern = dense_sparse_kernel<BITS, B, MODE>;
     static bool attr_set = false; // ask once for more than the default dynamic LDS
     if (!attr_set) {
+        const int static_lds = MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4;
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsBudget - (MODE != kSparseAdd ? kTableBytes : 0)) != hipSuccess)
+                                kLdsBudget - static_lds) != hipSuccess)
             (void)hipGetLastError(); // not fatal: launches within the default limit still work
         attr_set = true;
     }
-    if (ls.waves * 64 > max_threads<BITS, B, GW>()) return hipErrorInvalidConfiguration;
+    if (ls.waves < 1 || ls.waves > kMaxWaves) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(a.tiles * a.split)), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, a);
     return hipGetLastError();
 }
 
-template <int BITS, int MODE, int GW>
+template <int BITS, int MODE>
 hipError_t launch_batch(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
     switch (batch) {
-    case 1: return launch_one<BITS, 1, MODE, GW>(a, ls, stream);
-    case 2: return launch_one<BITS, 2, MODE, GW>(a, ls, stream);
-    case 3: return launch_one<BITS, 3, MODE, GW>(a, ls, stream);
-    case 4: return launch_one<BITS, 4, MODE, GW>(a, ls, stream);
-    case 5: return launch_one<BITS, 5, MODE, GW>(a, ls, stream);
-    case 6: return launch_one<BITS, 6, MODE, GW>(a, ls, stream);
-    case 7: return launch_one<BITS, 7, MODE, GW>(a, ls, stream);
-    case 8: return launch_one<BITS, 8, MODE, GW>(a, ls, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int BITS, int MODE>
-hipError_t launch_gw(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
-{
-    switch (ls.gw) {
-    case 1: return launch_batch<BITS, MODE, 1>(a, batch, ls, stream);
-    case 2: return launch_batch<BITS, MODE, 2>(a, batch, ls, stream);
-    case 3: return launch_batch<BITS, MODE, 3>(a, batch, ls, stream);
-    case 4: return launch_batch<BITS, MODE, 4>(a, batch, ls, stream);
+    case 1: return launch_one<BITS, 1, MODE>(a, ls, stream);
+    case 2: return launch_one<BITS, 2, MODE>(a, ls, stream);
+    case 3: return launch_one<BITS, 3, MODE>(a, ls, stream);
+    case 4: return launch_one<BITS, 4, MODE>(a, ls, stream);
+    case 5: return launch_one<BITS, 5, MODE>(a, ls, stream);
+    case 6: return launch_one<BITS, 6, MODE>(a, ls, stream);
+    case 7: return launch_one<BITS, 7, MODE>(a, ls, stream);
+    case 8: return launch_one<BITS, 8, MODE>(a, ls, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 } // namespace dev
 } // namespace sqllm
+
+#undef SQLLM_DOT
+#undef SQLLM_DOTS3
+#undef SQLLM_PAIR_OPERANDS
 
 #endif

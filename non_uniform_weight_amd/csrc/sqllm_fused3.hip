@@ -5,7 +5,7 @@ namespace sqllm {
 
 hipError_t launch_fused3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    return dev::launch_gw<3, kFused>(a, batch, ls, stream);
+    return dev::launch_batch<3, kFused>(a, batch, ls, stream);
 }
 
 } // namespace sqllm

@@ -16,7 +16,8 @@ constexpr int kMaxWaves = 16;     // waves per workgroup
 constexpr int kMaxSplit = 64;     // workgroups sharing one row tile
 constexpr int kTableBytes = 256 * 64 * 4;           // pair table: 256 entries x 64 lanes x half2
 constexpr int kLdsBudget = 160 * 1024;              // LDS per compute unit on gfx950
-constexpr int kSparseBatch = 4;   // 64-nonzero chunks a wave loads at once
+constexpr int kSparseShare = 512; // outlier nonzeros per wave the outlier-only kernel aims for
+constexpr int kDefaultWaves = 8;  // waves per workgroup: two workgroups share a compute unit
 
 enum Mode { kFused = 0, kDenseOnly = 1, kSparseAdd = 2 };
 
@@ -32,21 +33,14 @@ struct KernelArgs {
     int rows, cols, tiles, groups;
     int split;                // workgroups per row tile
     int gps;                  // column groups per workgroup (the last one may have fewer)
-    int gpw;                  // column groups per wave
-    int x_full;               // 1: every column of x is staged in LDS (outlier gathers read LDS)
+    int x_lds;                // 1: all of x staged in LDS for the outlier gathers
 };
 
 // One launch configuration, chosen on the host.
 struct LaunchShape {
     int waves;                // waves per workgroup
-    int gw;                   // compiled groups-per-wave capacity (1..4)
-    size_t dyn_lds;           // dynamic LDS bytes
+    size_t dyn_lds;           // dynamic LDS bytes (staged x)
 };
-
-// Most waves per workgroup a kernel holding gw groups of codes per wave and
-// `batch` accumulators is compiled for: 16 (128 VGPRs each) while codes plus
-// ~8 registers per batch column stay under 96 dwords, else 8.
-constexpr int max_waves(int bits, int batch, int gw) { return gw * 8 * bits + 8 * batch >= 96 ? 8 : 16; }
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
                                hipStream_t stream);
@@ -54,14 +48,13 @@ hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void 
 hipError_t launch_unpack(const void *packed, const uint16_t *lut, int rows, int cols, int bits, uint8_t *codes,
                          uint16_t *w, hipStream_t stream);
 
-// dynamic LDS of one workgroup: staged x (xgroups column groups of every
-// batch column), the tile's row pointers, per-wave outlier row sums
-inline size_t dynamic_lds_bytes(int xgroups, int batch, int waves, bool sparse)
-{
-    size_t b = (size_t)xgroups * kGroupCols * 2 * batch;
-    if (sparse) b += 68 * 4 + (size_t)waves * batch * kTileRows * 4;
-    return b;
-}
+// Dynamic LDS of a workgroup that stages x for the outlier gathers: every
+// column of every batch column.
+inline size_t staged_x_bytes(int64_t cols, int batch) { return (size_t)cols * batch * 2; }
+
+// Static LDS of a kernel: the pair table (dense modes) or the wave
+// reduction area (outlier-only mode).
+inline size_t static_lds_bytes(bool dense, int batch) { return dense ? kTableBytes : (size_t)kMaxWaves * batch * 64 * 4; }
 
 } // namespace sqllm
 

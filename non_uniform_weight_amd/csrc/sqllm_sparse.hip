@@ -5,9 +5,7 @@ namespace sqllm {
 
 hipError_t launch_spmv_add(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    LaunchShape one = ls;
-    one.gw = 1; // no code groups in this mode
-    return dev::launch_gw<3, kSparseAdd>(a, batch, one, stream);
+    return dev::launch_batch<3, kSparseAdd>(a, batch, ls, stream);
 }
 
 } // namespace sqllm
