@@ -43,15 +43,25 @@
  *   - rows >= 1; cols >= 256 and a multiple of 256; cols <= 65536 when
  *     outliers are given (16-bit column indices); nnz < 2^31; 1 <= batch <= 8.
  *
- * Packed code layout (the pages fix only "exactly b bits per index"; the
+ * Packed code layout (the pages fix only that every index takes exactly b bits; the
  * arrangement below is this library's, chosen so that each 64-lane wave
- * streams 1 KiB of codes per 128-bit load instruction):
+ * streams 1 KiB of codes per 128-bit load instruction and every code byte
+ * turns into a table address with one byte-permute):
  *   rows are grouped in tiles of 64 (tile t = r / 64, lane l = r % 64), the
  *   columns of a row in groups of 256 (g = c / 256, j = c % 256).  The 32*b
- *   bytes that hold the 256 codes of (r, g) form one little-endian bit
- *   string in which code j occupies bits [b*j, b*j + b).  That string is cut
- *   into 2*b pieces of 16 bytes; piece q of (r, g) is stored at byte offset
+ *   bytes that hold the 256 codes of (r, g) form the group's byte string,
+ *   cut into 2*b pieces of 16 bytes; piece q of (r, g) is stored at byte
  *       ((t * G + g) * 2b + q) * 1024 + l * 16,      G = cols / 256.
+ *   Codes go in pairs: pair p (0..127) holds codes 2p and 2p+1 as the
+ *   2b-bit value code[2p] | code[2p+1] << b.
+ *     4-bit: byte p of the string is pair p.
+ *     3-bit: the string is 8 units of 12 bytes; unit u holds pairs
+ *       16u .. 16u+15.  Pair 16u+p for p < 12 is the low six bits of unit
+ *       byte p.  Pair 16u+12+q (q = 0..3) stores its bits [2k, 2k+2) in the
+ *       top two bits of unit byte 4k + q, for k = 0, 1, 2.
+ *   Example (3-bit, codes 0,1,2,...,7 repeating along the row): the pair
+ *   values cycle 0x08, 0x1A, 0x2C, 0x3E, and every 12-byte unit reads
+ *   08 9A 2C BE 88 9A EC FE 08 5A AC FE.
  *   Rows of the last tile beyond `rows` are padding (zero after sqllm_pack).
  *   Total size: sqllm_packed_bytes() = ceil(rows / 64) * 64 * cols * b / 8.
  *   The packed buffer must be 16-byte aligned.

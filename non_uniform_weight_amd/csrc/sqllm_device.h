@@ -4,12 +4,12 @@
 // format").  Included by the translation units that instantiate it.
 //
 // One workgroup owns one row tile (64 rows, one per lane) and a range of its
-// 256-column groups.  Its waves take one of two roles:
+// 256-column groups.  Every wave does two kinds of work, interleaved:
 //
-//   dense waves stream packed codes.  The layout puts the same 16-byte piece
-//   of 64 consecutive rows side by side, so one wave-wide 128-bit load moves
-//   1 KiB of contiguous codes.  Each wave keeps a ring of `ring_depth` groups
-//   in flight (codes plus that group's activations) and computes one group
+//   dense groups: the layout puts the same 16-byte piece of 64 consecutive
+//   rows side by side, so one wave-wide 128-bit load moves 1 KiB of
+//   contiguous codes.  Each wave keeps a ring of `ring_depth` groups in
+//   flight (codes plus that group's activations) and computes one group
 //   while the next ones arrive.  A lookup reads the lane's own copy of its
 //   row's *pair* table in LDS: entry e holds the two centroids of code pair e
 //   as one half2 at byte (e << 8) | (lane << 2), so a lookup is one
@@ -22,14 +22,15 @@
 //   64+4n..64+4n+3) of the group, and v_dot2c_f32_f16 takes its x operand
 //   through a DPP row_newbcast:n, which hands lane n's pair to its whole row.
 //
-//   sparse waves take an even share of the tile's CSR nonzeros (balanced
-//   whatever the per-row skew: §3.4 "Kernel Implementation", balanced sparse
-//   kernel; Appendix C), 64 per lane-wide chunk, a round of chunks in flight
-//   at a time.  Each nonzero finds its row by a binary search over the
-//   tile's row pointers (held one per lane), gathers x (from LDS in the
-//   outlier-only kernel, which stages it there, else from the cache), and the
-//   products are summed per row by a segmented scan across the wave; each
-//   row's lane then fetches its sum.
+//   outlier chunks: the tile's CSR nonzeros are cut into even shares, one per
+//   wave of the split (balanced whatever the per-row skew: §3.4 "Kernel
+//   Implementation", balanced sparse kernel; Appendix C), 64 per lane-wide
+//   chunk, a round of chunks in flight at a time, one chunk after each dense
+//   group.  Within a chunk the rows are non-decreasing: each row that starts
+//   there marks its first lane, a ballot of the marks gives every lane its
+//   segment start, x is gathered (from LDS when it is staged there, else
+//   through the cache), and a DPP segmented scan sums each row's products;
+//   the row's own lane fetches its sum.
 //
 // The waves' fp32 row sums are added in a fixed order; the sparse part joins
 // the dense part in fp32 before the single rounding (kernel fusion).  A row
@@ -37,6 +38,7 @@
 // sums into a (sum, count) word per output with a compare-and-swap and the
 // one that completes the count rounds and writes y -- no fences or cache
 // flushes, one atomic round trip.
+
 #ifndef SQLLM_DEVICE_H
 #define SQLLM_DEVICE_H
 

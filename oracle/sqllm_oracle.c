@@ -30,7 +30,7 @@
  * adding duplicates.
  *
  * Packed layout read by oracle_unpack (the storage format of the library;
- * the pages fix only "exactly b bits per index", the rest is this library's
+ * the pages fix only that every index takes exactly b bits; the rest is this library's
  * choice):
  *   tiles of 64 rows (t = r / 64, lane l = r % 64), groups of 256 columns
  *   (g = c / 256, j = c % 256), 2b pieces of 16 bytes per (row, group).

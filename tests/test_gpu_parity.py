@@ -344,3 +344,56 @@ def test_workload4(batch):
         m = synth.make_matrix(spec, seed=0, workload=4, index=i)
         sel = None if batch == 1 else np.sort(rng.choice(spec.rows, 2048, replace=False))
         _check_matrix(m, sel)
+
+
+@pytest.mark.parametrize("bits,density_bp", [(3, 0), (3, 5), (3, 45), (4, 0), (4, 5), (4, 45)])
+def test_workload5_layer_sample(bits, density_bp):
+    """The 80-layer stream at full size: its last layer's 7 linears (the
+    stream's matrix indices 553..559, as the benchmark draws them), one
+    workspace shared by all calls as in the benchmark, 2048 sampled rows of
+    each checked against the oracle."""
+    specs = synth.workload(5, bits=bits, density_bp=density_bp)
+    rng = np.random.default_rng(stable_seed("w5", bits, density_bp))
+    ws = torch.zeros(nw().workspace_bytes(22016, 22016, 1), dtype=torch.uint8, device="cuda")
+    for i in range(len(specs) - 7, len(specs)):
+        spec = specs[i]
+        step(f"workload 5 bits {bits} density {density_bp}bp matrix {i} {spec}")
+        m = synth.make_matrix(spec, seed=0, workload=5, index=i)
+        assert m.col.size == spec.nnz
+        sel = np.sort(rng.choice(spec.rows, 2048, replace=False))
+        _check_matrix(m, sel, ws=ws)
+
+
+def test_graph_replay_matches_eager():
+    """The benchmark times HIP-graph replays of the fused call: a captured
+    sequence of calls sharing one workspace gives, on every replay, the bits
+    of the same calls made eagerly."""
+    specs = [synth.MatrixSpec("q", 8192, 8192, 3), synth.MatrixSpec("gate", 22016, 8192, 3),
+             synth.MatrixSpec("down", 8192, 22016, 3), synth.MatrixSpec("small", 4096, 4096, 4, 1, 5)]
+    ws = torch.zeros(nw().workspace_bytes(22016, 22016, 1), dtype=torch.uint8, device="cuda")
+    mats = []
+    for i, spec in enumerate(specs):
+        step(f"graph replay: prepare {spec}")
+        mats.append(DevMatrix.from_synth(synth.make_matrix(spec, seed=3, workload=5, index=i)))
+    eager = [d.fused(ws=ws) for d in mats]
+    torch.cuda.synchronize()
+    eager = [dev_to_u16(y) for y in eager]
+    outs = [torch.empty((1, d.rows), dtype=torch.float16, device="cuda") for d in mats]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    step("graph replay: capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for d, y in zip(mats, outs):
+                d.fused(y=y, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        step(f"graph replay {rep}")
+        for y in outs:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (y, ref) in enumerate(zip(outs, eager)):
+            assert np.array_equal(dev_to_u16(y), ref), f"replay {rep} matrix {k} differs from the eager call"
