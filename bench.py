@@ -3,9 +3,13 @@
 
 One step = one pass over the whole weight stream of an 80-layer
 LLaMA-65B-shaped model at batch 1: 80 x (q, k, v, o 8192x8192; gate, up
-22016x8192; down 8192x22016) = 560 calls of sqllm_dense_sparse_gemv, 3-bit
-codes with per-row 8-entry fp16 tables and 0.45% fp16 CSR outliers, each with
-its own fp16 activation vector, back to back on one stream.  Inputs are seeded
+22016x8192; down 8192x22016) = 560 fused products, 3-bit codes with per-row
+8-entry fp16 tables and 0.45% fp16 CSR outliers, each with its own fp16
+activation vector, back to back on one stream.  A decoder layer can compute
+q, k and v together (one input) and gate and up together (one input), so the
+default launch order is four launches of sqllm_dense_sparse_gemv_group per
+layer: (q, k, v), (o), (gate, up), (down); `--launch single` makes one
+sqllm_dense_sparse_gemv call per product instead.  Inputs are seeded
 synthetic data of those shapes and distributions (no trained weights), all
 resident in HBM before the timed region (24.3 GB of codes + 1.2 GB of CSR).
 
@@ -47,6 +51,8 @@ def parse():
     p.add_argument("--layers", type=int, default=80)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-graph", action="store_true", help="time plain launches only")
+    p.add_argument("--launch", choices=("level", "single"), default="level",
+                   help="level: one group launch per (q,k,v), (o), (gate,up), (down); single: one call per product")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -73,7 +79,8 @@ class WeightStream:
         rows_max = max(s.rows for s in specs)
         cols_max = max(s.cols for s in specs)
         batch = max(s.batch for s in specs)
-        self.ws = torch.zeros(max(nw.workspace_bytes(rows_max, cols_max, batch), 256), dtype=torch.uint8,
+        # a group launch gives every product its own slots: room for three
+        self.ws = torch.zeros(max(3 * nw.workspace_bytes(rows_max, cols_max, batch), 256), dtype=torch.uint8,
                               device="cuda")
         t0 = time.time()
         for i, spec in enumerate(specs):
@@ -101,10 +108,31 @@ class WeightStream:
         torch.cuda.synchronize()
         self._marshal()
 
+    LEVELS = ((0, 1, 2), (3,), (4, 5), (6,))  # per layer: (q, k, v), (o), (gate, up), (down)
+
     def _marshal(self):
         lib = self.nw.library()
         self.fn = lib.sqllm_dense_sparse_gemv
+        self.group_fn = lib.sqllm_dense_sparse_gemv_group
         vp = ctypes.c_void_p
+        self.groups = []
+        for l0 in range(0, len(self.mats), 7):
+            for lv in self.LEVELS:
+                ids = [l0 + i for i in lv if l0 + i < len(self.mats)]
+                if not ids:
+                    continue
+                arr = (self.nw.Product * len(ids))()
+                for k, i in enumerate(ids):
+                    d = self.mats[i]
+                    sp, nnz = d["spec"], d["nnz"]
+                    arr[k] = self.nw.Product(d["packed"].data_ptr(), d["lut"].data_ptr(),
+                                             d["row_ptr"].data_ptr() if nnz else None,
+                                             d["col"].data_ptr() if nnz else None,
+                                             d["val"].data_ptr() if nnz else None, nnz, sp.rows, sp.cols,
+                                             d["x"].data_ptr(), d["y"].data_ptr())
+                need = int(lib.sqllm_group_workspace_bytes(arr, len(ids), self.specs[ids[0]].batch))
+                assert 0 < need <= self.ws.numel(), (need, self.ws.numel())
+                self.groups.append((arr, len(ids), self.specs[ids[0]].batch))
         self.calls = []
         for d in self.mats:
             s = d["spec"]
@@ -124,10 +152,18 @@ class WeightStream:
             if st != 0:
                 raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
 
+    def step_grouped(self, stream) -> None:
+        fn, h = self.group_fn, vp_stream(stream)
+        ws, wsb = ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel()
+        for arr, n, batch in self.groups:
+            st = fn(arr, n, self.bits, batch, ws, wsb, h)
+            if st != 0:
+                raise RuntimeError(f"sqllm_dense_sparse_gemv_group failed with status {st}")
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the kernel sources as they are now (else None)."""
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    if it was taken on the kernel sources as they are now (else None)."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -143,7 +179,8 @@ def measured_traffic():
                 if " = " in line:
                     k, v = line.rsplit(" = ", 1)
                     fields[k.strip().split()[-1]] = v.strip()
-        if fields.get("kernel_sources_sha256") == sha and "traffic_bytes_per_launch" in fields:
+        if (fields.get("kernel_sources_sha256") == sha and fields.get("roofline_kernel") == kernel
+                and "traffic_bytes_per_launch" in fields):
             return int(float(fields["traffic_bytes_per_launch"]))
     return None
 
@@ -202,44 +239,56 @@ def main():
     torch.cuda.set_device(0)
     specs = synth.workload(5, bits=args.bits, density_bp=args.density_bp)[:7 * args.layers]
     ws = WeightStream(specs, args.seed)
-    n_calls = len(ws.calls)
+    n_products = len(ws.calls)
     stream = torch.cuda.Stream()
 
-    # One step = all GEMVs of the stream, launched back to back on one stream,
-    # captured once in a HIP graph (plain launches with --no-graph).
-    def run_step():
-        ws.step(stream)
+    def time_mode(step_fn):
+        """ms per step: W warm-up steps, then K timed steps between events on
+        the launch stream; one step = every product of the stream, launched
+        back to back, captured once in a HIP graph (plain launches with
+        --no-graph)."""
+        def run_step():
+            step_fn(stream)
 
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            ws.step(stream)
-        run_step = g.replay
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):  # replay() launches on the current stream
-        for _ in range(args.warmup):
-            run_step()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            run_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+        if not args.no_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step_fn(stream)
+            run_step = g.replay
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            for _ in range(args.warmup):
+                run_step()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                run_step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
     mode = "plain launches" if args.no_graph else "HIP graph replay"
-    log(f"{mode}: {ms:.3f} ms/step")
+    single_ms = time_mode(ws.step)
+    log(f"single calls, {mode}: {single_ms:.3f} ms/step ({single_ms * 1e3 / n_products:.2f} us/product)")
+    if args.launch == "level":
+        ms = time_mode(ws.step_grouped)
+        n_launches = len(ws.groups)
+        kernel = f"dense_sparse_group_kernel<{args.bits},1,fused>"
+        log(f"group launches, {mode}: {ms:.3f} ms/step ({n_launches} launches)")
+    else:
+        ms, n_launches, kernel = single_ms, n_products, f"dense_sparse_kernel<{args.bits},1,fused>"
 
     value = ws.bytes_per_step / (ms * 1e-3) / 1e9
-    # every launch runs the same kernel (the fused 3/4-bit product); its
-    # average duration is the timed region's length over the launches in it
-    avg_launch_ms = ms / n_calls
-    avg_bytes = ws.bytes_per_step / n_calls
+    # every launch of the step runs the same kernel; its average duration is
+    # the timed region's length over the launches in it
+    avg_launch_ms = ms / n_launches
+    avg_bytes = ws.bytes_per_step / n_launches
     achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
     log(f"per launch: {avg_launch_ms * 1e3:.2f} us avg, {achieved:.0f} GB/s")
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
-    traffic = measured_traffic() if args.bits == 3 and args.density_bp == 45 else None
+    traffic = measured_traffic(kernel) if args.bits == 3 and args.density_bp == 45 else None
     cpu = None
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
@@ -260,21 +309,25 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"80-layer LLaMA-65B-shaped weight stream, {n_calls} GEMVs "
+            "workload": f"80-layer LLaMA-65B-shaped weight stream, {n_products} GEMVs "
                         f"(8192x8192 x4, 22016x8192 x2, 8192x22016 per layer), {args.bits}-bit codes, "
                         f"{args.density_bp / 100:.2f}% uniform CSR outliers, batch 1",
             "bits": args.bits,
             "outlier_density_pct": args.density_bp / 100,
             "batch": 1,
-            "gemvs_per_step": n_calls,
+            "gemvs_per_step": n_products,
             "bytes_per_step": ws.bytes_per_step,
-            "launch": mode,
+            "launch": mode + (", one group launch per (q,k,v), (o), (gate,up), (down)" if args.launch == "level"
+                              else ", one call per product"),
         },
-        "us_per_gemv": round(ms * 1e3 / n_calls, 3),
+        "us_per_gemv": round(ms * 1e3 / n_products, 3),
+        "single_calls": {"value": round(ws.bytes_per_step / (single_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                         "us_per_gemv": round(single_ms * 1e3 / n_products, 3)},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"dense_sparse_kernel<{args.bits},1,fused>",
+            "kernel": kernel,
+            "launches_per_step": n_launches,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

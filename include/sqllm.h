@@ -169,6 +169,44 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
                                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sqllm_dense_sparse_gemv_group -- n independent fused products
+ * y_i = (D_i + S_i) x_i in one launch (1 <= n <= 8), all with the same
+ * `bits` and `batch`: for instance the query, key and value projections of
+ * one attention block, or the gate and up projections of one MLP, which the
+ * pages' decoder layers (§5 "Experiments", LLaMA) compute from one input.
+ * Each product is the one sqllm_dense_sparse_gemv computes, within the same
+ * tolerance; the launch lets one product's start-up and tail overlap the
+ * others' code streams.
+ *   items: HOST array of n descriptors (read during the call only); each
+ *          holds device pointers laid out as for sqllm_dense_sparse_gemv,
+ *          nnz == 0 allowed (row_ptr / col_idx / val may then be NULL).
+ *          No product's y may overlap any product's inputs or another y.
+ *   workspace: at least sqllm_group_workspace_bytes(items, n, batch) bytes,
+ *          256-byte aligned, zero-filled before first use, left zeroed; the
+ *          products use disjoint parts of it in item order.
+ * Products with and without outliers are launched separately (at most two
+ * launches, in stream order).  Argument errors are reported before any
+ * launch.
+ */
+typedef struct {
+    const void *packed;       /* sqllm_pack output, 16-byte aligned */
+    const uint16_t *lut;      /* fp16 [rows][2^bits], 16-byte aligned */
+    const int32_t *row_ptr;   /* int32 [rows + 1] */
+    const uint16_t *col_idx;  /* uint16 [nnz] */
+    const uint16_t *val;      /* fp16 [nnz] */
+    int64_t nnz;
+    int64_t rows;
+    int64_t cols;
+    const uint16_t *x;        /* fp16 [batch][cols], 16-byte aligned */
+    uint16_t *y;              /* fp16 [batch][rows], overwritten */
+} sqllm_product;
+
+size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch);
+
+sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, int bits, int batch, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Test-only exports (not part of the stable contract).  The readers are
  * asynchronous on `stream`.
  *   sqllm_test_unpack: packed -> uint8 codes [rows][cols]

@@ -43,6 +43,18 @@ _lib.sqllm_spmv_add.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
 _lib.sqllm_dense_sparse_gemv.restype = _i32
 _lib.sqllm_dense_sparse_gemv.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                          _sz, _vp]
+
+
+class Product(ctypes.Structure):
+    """One item of sqllm_dense_sparse_gemv_group (sqllm_product)."""
+    _fields_ = [("packed", _vp), ("lut", _vp), ("row_ptr", _vp), ("col_idx", _vp), ("val", _vp), ("nnz", _i64),
+                ("rows", _i64), ("cols", _i64), ("x", _vp), ("y", _vp)]
+
+
+_lib.sqllm_group_workspace_bytes.restype = _sz
+_lib.sqllm_group_workspace_bytes.argtypes = [ctypes.POINTER(Product), _i32, _i32]
+_lib.sqllm_dense_sparse_gemv_group.restype = _i32
+_lib.sqllm_dense_sparse_gemv_group.argtypes = [ctypes.POINTER(Product), _i32, _i32, _i32, _vp, _sz, _vp]
 _lib.sqllm_test_unpack.restype = _i32
 _lib.sqllm_test_unpack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
 _lib.sqllm_test_tuning.restype = _i32
@@ -51,8 +63,9 @@ _lib.sqllm_test_decode.restype = _i32
 _lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
 
 EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes", "sqllm_pack", "sqllm_gemv",
-           "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_test_unpack", "sqllm_test_decode",
-           "sqllm_test_tuning")
+           "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_group_workspace_bytes",
+           "sqllm_dense_sparse_gemv_group", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning")
+MAX_GROUP = 8
 
 SQLLM_OK = 0
 
@@ -104,8 +117,12 @@ _WORKSPACES: dict = {}
 def workspace(rows: int, cols: int, batch: int, device=None) -> torch.Tensor:
     """Zero-filled workspace cached per device (grown on demand).  Calls that
     share it must be ordered on one stream."""
+    return _cached_workspace(workspace_bytes(rows, cols, batch), device)
+
+
+def _cached_workspace(nbytes: int, device=None) -> torch.Tensor:
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    need = max(workspace_bytes(rows, cols, batch), 256)
+    need = max(nbytes, 256)
     ws = _WORKSPACES.get(device)
     if ws is None or ws.numel() < need:
         ws = torch.zeros(need, dtype=torch.uint8, device=device)
@@ -182,6 +199,41 @@ def dense_sparse_gemv(packed, lut, bits, row_ptr, col, val, x, y=None, ws=None, 
                                         _dev(y, "y", torch.float16), _dev(ws, "workspace", torch.uint8), ws.numel(),
                                         _stream(stream)), "sqllm_dense_sparse_gemv")
     return y
+
+
+def group_products(items, bits: int):
+    """ctypes array of sqllm_product from dicts with keys packed, lut, row_ptr,
+    col, val, x, y (tensors; row_ptr/col/val may be None)."""
+    arr = (Product * len(items))()
+    batch = None
+    for k, it in enumerate(items):
+        rows = it["lut"].shape[0]
+        x, y, b, cols = _x_y(it["x"], it["y"], rows)
+        if batch is not None and b != batch:
+            raise ValueError("group: every product must have the same batch")
+        batch = b
+        rp, ci, cv, nnz = _csr_ptrs(it.get("row_ptr"), it.get("col"), it.get("val"))
+        arr[k] = Product(_dev(it["packed"], "packed", torch.uint8), _dev(it["lut"], "lut", torch.float16), rp, ci, cv,
+                         nnz, rows, cols, _dev(x, "x", torch.float16), _dev(y, "y", torch.float16))
+    return arr, batch
+
+
+def group_workspace_bytes(items, bits: int) -> int:
+    arr, batch = group_products(items, bits)
+    return int(_lib.sqllm_group_workspace_bytes(arr, len(items), batch))
+
+
+def dense_sparse_gemv_group(items, bits: int, ws: torch.Tensor | None = None, stream=None) -> None:
+    """y_i = (D_i + S_i) x_i for up to 8 independent products in one launch.
+    items: dicts with packed, lut, row_ptr, col, val, x and y (y preallocated
+    fp16 [batch, rows]); ws: zero-filled uint8 workspace of at least
+    group_workspace_bytes(items, bits) bytes (a cached one if None)."""
+    arr, batch = group_products(items, bits)
+    need = int(_lib.sqllm_group_workspace_bytes(arr, len(items), batch))
+    if ws is None:
+        ws = _cached_workspace(need, items[0]["x"].device)
+    _check(_lib.sqllm_dense_sparse_gemv_group(arr, len(items), bits, batch, _dev(ws, "workspace", torch.uint8),
+                                              ws.numel(), _stream(stream)), "sqllm_dense_sparse_gemv_group")
 
 
 def unpack_codes(packed, rows, cols, bits, stream=None) -> torch.Tensor:

@@ -67,12 +67,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // at least min_gps groups each.  With
 // outliers x is staged in LDS when it fits beside the pair table -- for two
 // workgroups per compute unit when there are more workgroups than units.
-void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
+// total_tiles: row tiles of every product sharing the launch.
+void choose_split(KernelArgs &a, int64_t total_tiles)
 {
-    const int64_t T = a.tiles, G = a.groups;
+    const int64_t G = a.groups;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        s = ceil_div(tuning().target_wgs, T);
+        s = ceil_div(tuning().target_wgs, total_tiles);
         int64_t cap = G / tuning().min_gps;
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
@@ -83,19 +84,36 @@ void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
     const int gps = (int)ceil_div(G, s);
     a.split = (int)ceil_div(G, gps); // no empty splits
     a.gps = gps;
-    // one workgroup per compute unit: 16 waves; more workgroups than units:
-    // 8 waves, two workgroups per unit
-    const bool two_per_cu = T * a.split > tuning().target_wgs;
-    ls.waves = tuning().force_waves ? tuning().force_waves : (two_per_cu ? kDefaultWaves : kMaxWaves);
+}
+
+// One workgroup per compute unit: 16 waves; more workgroups than units: 8
+// waves, two workgroups per unit.
+int choose_waves(int64_t workgroups)
+{
+    if (tuning().force_waves) return tuning().force_waves;
+    return workgroups > tuning().target_wgs ? kDefaultWaves : kMaxWaves;
+}
+
+// Stage x in LDS for the outlier gathers when it fits beside the pair table
+// (in half of the LDS when two workgroups share a unit).
+void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int waves, LaunchShape &ls)
+{
     a.x_lds = 0;
-    ls.dyn_lds = 0;
-    if (nnz > 0) {
-        const size_t lds = kTableBytes + staged_x_bytes(a.cols, batch);
-        if (lds <= (size_t)(two_per_cu ? kLdsBudget / 2 : kLdsBudget)) {
-            a.x_lds = 1;
-            ls.dyn_lds = staged_x_bytes(a.cols, batch);
-        }
+    if (nnz <= 0) return;
+    const size_t staged = staged_x_bytes(a.cols, batch);
+    const size_t budget = waves <= kDefaultWaves ? kLdsBudget / 2 : kLdsBudget;
+    if (kTableBytes + staged <= budget) {
+        a.x_lds = 1;
+        if (staged > ls.dyn_lds) ls.dyn_lds = staged;
     }
+}
+
+void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
+{
+    choose_split(a, a.tiles);
+    ls.waves = choose_waves((int64_t)a.tiles * a.split);
+    ls.dyn_lds = 0;
+    choose_x_lds(a, batch, nnz, ls.waves, ls);
 }
 
 // Outlier-only kernel: about kSparseShare nonzeros per wave; x staged in LDS
@@ -266,6 +284,78 @@ sqllm_status sqllm_spmv_add(const int32_t *row_ptr, const uint16_t *col_idx, con
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
     if (launch_dense_sparse(a, 3, batch, kSparseAdd, ls, stream) != hipSuccess) return SQLLM_ERR_HIP;
+    return SQLLM_OK;
+}
+
+size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch)
+{
+    if (!items || n < 1 || n > kMaxGroup || batch < 1 || batch > kMaxBatch) return 0;
+    size_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        if (check_shape(items[i].rows, items[i].cols) != SQLLM_OK) return 0;
+        total += workspace_need(items[i].rows, batch);
+    }
+    return total;
+}
+
+sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, int bits, int batch, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream)
+{
+    if (!items) return SQLLM_ERR_NULL;
+    if (n < 1 || n > kMaxGroup) return SQLLM_ERR_SHAPE;
+    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (batch < 1 || batch > kMaxBatch) return SQLLM_ERR_BATCH;
+    // every product's arguments first, as for the single call
+    for (int i = 0; i < n; ++i) {
+        const sqllm_product &p = items[i];
+        if (!p.packed || !p.lut) return SQLLM_ERR_NULL;
+        sqllm_status st = common_checks(p.rows, p.cols, p.x, batch, p.y);
+        if (st != SQLLM_OK) return st;
+        st = sparse_checks(p.row_ptr, p.col_idx, p.val, p.nnz, p.cols);
+        if (st != SQLLM_OK) return st;
+        if (!aligned(p.packed, 16) || !aligned(p.lut, 16)) return SQLLM_ERR_ALIGN;
+    }
+    if (workspace && !aligned(workspace, 256)) return SQLLM_ERR_WORKSPACE;
+    // products with outliers run in one launch, those without in another
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool fused = pass == 0;
+        GroupArgs g{};
+        int64_t total_tiles = 0;
+        for (int i = 0; i < n; ++i)
+            if ((items[i].nnz > 0) == fused) total_tiles += tiles_of(items[i].rows);
+        if (total_tiles == 0) continue;
+        size_t ws_off = 0;
+        int64_t wgs = 0;
+        for (int i = 0; i < n; ++i) {
+            const sqllm_product &p = items[i];
+            const size_t need = workspace_need(p.rows, batch); // every product has its own slots
+            if ((p.nnz > 0) != fused) {
+                ws_off += need;
+                continue;
+            }
+            KernelArgs a = base_args(p.rows, p.cols, p.x, p.y,
+                                     workspace ? (void *)((char *)workspace + ws_off) : nullptr);
+            ws_off += need;
+            a.packed = p.packed;
+            a.lut = p.lut;
+            a.row_ptr = p.row_ptr;
+            a.col = p.col_idx;
+            a.val = p.val;
+            choose_split(a, total_tiles);
+            if (a.split > 1 && (!workspace || workspace_bytes < ws_off)) return SQLLM_ERR_WORKSPACE;
+            g.item[g.n] = a;
+            g.first[g.n] = (int)wgs;
+            wgs += (int64_t)a.tiles * a.split;
+            ++g.n;
+        }
+        if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
+        g.first[g.n] = (int)wgs;
+        LaunchShape ls{};
+        ls.waves = choose_waves(wgs);
+        for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);
+        if (launch_dense_sparse_group(g, bits, batch, fused ? kFused : kDenseOnly, ls, stream) != hipSuccess)
+            return SQLLM_ERR_HIP;
+    }
     return SQLLM_OK;
 }
 

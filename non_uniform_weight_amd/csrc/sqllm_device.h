@@ -598,7 +598,7 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
 // (placeholders past the wave's last group), so the wait before each group's
 // math lets exactly D-1 groups stay in flight.
 template <int BITS, int B, int MODE>
-__global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs a)
+__device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 {
     constexpr bool DENSE = MODE != kSparseAdd;
     constexpr bool SPARSE = MODE != kDenseOnly;
@@ -613,7 +613,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
     const int W = nt >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x / a.split, s = blockIdx.x - t * a.split;
+    const int t = bid / a.split, s = bid - t * a.split;
     const int row0 = t * 64;
     const uint32_t lane4 = (uint32_t)lane << 2;
 
@@ -632,15 +632,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
         }
     }
 
-    // -- 2. small loads first: the tile's row pointers, this thread's table
-    //       items and quads of x to stage
+    // -- 2. small loads first: this thread's table rows (ahead of every other
+    //       load: the table is what the first group's math waits for), the
+    //       tile's row pointers and quads of x to stage
+    TableItems<BITS, ITEMS> items; // loaded by every thread (no branch), stored by those that own items
+    if constexpr (DENSE) {
+        table_items_load<BITS, ITEMS>(items, a.lut, threadIdx.x, nt, row0, a.rows);
+        asm volatile("" ::: "memory"); // the loads may not sink below this point
+    }
     int rp_lo = 0, rp_hi = 0;
     if constexpr (SPARSE) {
         rp_lo = a.row_ptr[min(row0 + lane, a.rows)];
         rp_hi = a.row_ptr[min(row0 + lane + 1, a.rows)];
     }
-    TableItems<BITS, ITEMS> items; // loaded by every thread (no branch), stored by those that own items
-    if constexpr (DENSE) table_items_load<BITS, ITEMS>(items, a.lut, threadIdx.x, nt, row0, a.rows);
     const int nxq = (SPARSE && a.x_lds) ? B * (a.cols >> 3) : 0; // 16-byte quads of x to stage
     u32x4 xq[SPARSE ? kStageQuads : 1];
     if constexpr (SPARSE) {
@@ -797,6 +801,27 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
 }
 
 template <int BITS, int B, int MODE>
+__global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs a)
+{
+    product_body<BITS, B, MODE>(a, blockIdx.x);
+}
+
+// Several independent products in one launch: workgroups [first[i],
+// first[i+1]) run product i.  The hardware starts a workgroup as soon as a
+// compute unit has room, so one product's start-up (table loads) and tail
+// (reductions) overlap the other products' code streams.
+template <int BITS, int B, int MODE>
+__global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(GroupArgs g)
+{
+    const int bid = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxGroup; ++k)
+        if (k < g.n && bid >= g.first[k]) i = k;
+    product_body<BITS, B, MODE>(g.item[i], bid - g.first[i]);
+}
+
+template <int BITS, int B, int MODE>
 hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
     auto kern = dense_sparse_kernel<BITS, B, MODE>;
@@ -812,6 +837,39 @@ hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t st
     const dim3 grid((unsigned)(a.tiles * a.split)), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, a);
     return hipGetLastError();
+}
+
+template <int BITS, int B, int MODE>
+hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
+{
+    auto kern = dense_sparse_group_kernel<BITS, B, MODE>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsBudget - kTableBytes) != hipSuccess)
+            (void)hipGetLastError();
+        attr_set = true;
+    }
+    if (ls.waves < 1 || ls.waves > kMaxWaves || g.n < 1 || g.n > kMaxGroup) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)g.first[g.n]), block((unsigned)(64 * ls.waves));
+    hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, g);
+    return hipGetLastError();
+}
+
+template <int BITS, int MODE>
+hipError_t launch_group_batch(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    switch (batch) {
+    case 1: return launch_group_one<BITS, 1, MODE>(g, ls, stream);
+    case 2: return launch_group_one<BITS, 2, MODE>(g, ls, stream);
+    case 3: return launch_group_one<BITS, 3, MODE>(g, ls, stream);
+    case 4: return launch_group_one<BITS, 4, MODE>(g, ls, stream);
+    case 5: return launch_group_one<BITS, 5, MODE>(g, ls, stream);
+    case 6: return launch_group_one<BITS, 6, MODE>(g, ls, stream);
+    case 7: return launch_group_one<BITS, 7, MODE>(g, ls, stream);
+    case 8: return launch_group_one<BITS, 8, MODE>(g, ls, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int BITS, int MODE>

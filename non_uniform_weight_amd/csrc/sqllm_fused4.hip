@@ -8,4 +8,9 @@ hipError_t launch_fused4(const KernelArgs &a, int batch, const LaunchShape &ls, 
     return dev::launch_batch<4, kFused>(a, batch, ls, stream);
 }
 
+hipError_t launch_group_fused4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_group_batch<4, kFused>(g, batch, ls, stream);
+}
+
 } // namespace sqllm

@@ -8,4 +8,9 @@ hipError_t launch_gemv4(const KernelArgs &a, int batch, const LaunchShape &ls, h
     return dev::launch_batch<4, kDenseOnly>(a, batch, ls, stream);
 }
 
+hipError_t launch_group_gemv4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_group_batch<4, kDenseOnly>(g, batch, ls, stream);
+}
+
 } // namespace sqllm

@@ -36,6 +36,14 @@ struct KernelArgs {
     int x_lds;                // 1: all of x staged in LDS for the outlier gathers
 };
 
+// Independent products run by one launch (same bits and batch).
+constexpr int kMaxGroup = 8;
+struct GroupArgs {
+    int n;                        // products
+    int first[kMaxGroup + 1];     // first workgroup of product i; first[n] = grid size
+    KernelArgs item[kMaxGroup];
+};
+
 // One launch configuration, chosen on the host.
 struct LaunchShape {
     int waves;                // waves per workgroup
@@ -44,6 +52,8 @@ struct LaunchShape {
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
                                hipStream_t stream);
+hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mode mode, const LaunchShape &ls,
+                                     hipStream_t stream);
 hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void *packed, int *bad, hipStream_t stream);
 hipError_t launch_unpack(const void *packed, const uint16_t *lut, int rows, int cols, int bits, uint8_t *codes,
                          uint16_t *w, hipStream_t stream);

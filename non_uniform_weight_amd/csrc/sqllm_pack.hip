@@ -20,6 +20,10 @@ hipError_t launch_fused4(const KernelArgs &a, int batch, const LaunchShape &ls, 
 hipError_t launch_gemv3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_gemv4(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_spmv_add(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_fused3(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_fused4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_gemv3(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_gemv4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
                                hipStream_t stream)
@@ -28,6 +32,19 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
     case kFused: return bits == 3 ? launch_fused3(a, batch, ls, stream) : launch_fused4(a, batch, ls, stream);
     case kDenseOnly: return bits == 3 ? launch_gemv3(a, batch, ls, stream) : launch_gemv4(a, batch, ls, stream);
     case kSparseAdd: return launch_spmv_add(a, batch, ls, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mode mode, const LaunchShape &ls,
+                                     hipStream_t stream)
+{
+    switch (mode) {
+    case kFused:
+        return bits == 3 ? launch_group_fused3(g, batch, ls, stream) : launch_group_fused4(g, batch, ls, stream);
+    case kDenseOnly:
+        return bits == 3 ? launch_group_gemv3(g, batch, ls, stream) : launch_group_gemv4(g, batch, ls, stream);
+    case kSparseAdd: break;
     }
     return hipErrorInvalidValue;
 }

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
@@ -119,6 +119,47 @@ def test_pack_and_reader_argument_errors(lib):
     assert lib.sqllm_test_unpack(A16, 64, 256, 3, None, None) == 1
     assert lib.sqllm_test_decode(A16, None, 64, 256, 3, B16, None) == 1
     assert lib.sqllm_test_decode(A16, B16, 64, 256, 2, B16, None) == 2
+
+
+def _products(nwpkg, n, **over):
+    arr = (nwpkg.Product * max(n, 1))()
+    for k in range(max(n, 1)):
+        f = dict(packed=A16.value, lut=B16.value, row_ptr=A16.value, col_idx=A16.value, val=A16.value, nnz=10,
+                 rows=64, cols=256, x=A16.value, y=B16.value)
+        f.update(over)
+        arr[k] = nwpkg.Product(**f)
+    return arr
+
+
+def group(lib, nwpkg, n=2, bits=3, batch=1, ws=A16, wsb=1 << 20, **over):
+    return lib.sqllm_dense_sparse_gemv_group(_products(nwpkg, n, **over), n, bits, batch, ws, wsb, None)
+
+
+def test_group_argument_errors(lib, nwpkg):
+    assert lib.sqllm_dense_sparse_gemv_group(None, 2, 3, 1, A16, 1 << 20, None) == 1
+    assert group(lib, nwpkg, n=0) == 3
+    assert group(lib, nwpkg, n=9) == 3
+    assert group(lib, nwpkg, bits=2) == 2
+    assert group(lib, nwpkg, batch=9) == 4
+    assert group(lib, nwpkg, packed=None) == 1
+    assert group(lib, nwpkg, x=None) == 1
+    assert group(lib, nwpkg, row_ptr=None) == 1
+    assert group(lib, nwpkg, cols=300) == 3
+    assert group(lib, nwpkg, nnz=-1) == 3
+    assert group(lib, nwpkg, x=MIS.value) == 5
+    assert group(lib, nwpkg, lut=0x100004) == 5
+    assert group(lib, nwpkg, ws=P(0x100010)) == 8
+    # split workgroups need the workspace: one tile of 8192 columns is split
+    assert group(lib, nwpkg, n=1, cols=8192, ws=None) == 8
+    assert group(lib, nwpkg, n=1, cols=8192, wsb=16) == 8
+
+
+def test_group_workspace_bytes(lib, nwpkg):
+    arr = _products(nwpkg, 3, rows=100)
+    assert lib.sqllm_group_workspace_bytes(arr, 3, 2) == 3 * nwpkg.workspace_bytes(100, 256, 2)
+    assert lib.sqllm_group_workspace_bytes(arr, 0, 1) == 0
+    assert lib.sqllm_group_workspace_bytes(arr, 3, 9) == 0
+    assert lib.sqllm_group_workspace_bytes(_products(nwpkg, 2, cols=100), 2, 1) == 0
 
 
 def test_tuning_hook_bounds(lib):
