@@ -44,6 +44,7 @@ Tuning &tuning_state()
 
 const Tuning &tuning() { return tuning_state(); }
 
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int64_t tiles_of(int64_t rows) { return (rows + kTileRows - 1) / kTileRows; }

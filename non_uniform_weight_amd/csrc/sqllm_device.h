@@ -84,6 +84,15 @@ struct Format {
 template <int K>
 constexpr uint32_t addr_sel() { return 0x0C0C0000u | ((4u + K) << 8); }
 
+// (a & mask) | (b & ~mask) as one v_bfi_b32 (written out, the compiler
+// turns it back into separate masks).
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+    return r;
+}
+
 // Pair-table byte address of pair P (0..127) of a group held in d[].
 template <int BITS, int P>
 __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lane4)
@@ -95,9 +104,12 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
         if constexpr (pu < 12) {
             return __builtin_amdgcn_perm(d[3 * u + pu / 4], lane4, addr_sel<pu % 4>());
         } else {
-            // pair 12+q of the unit: bits [2k, 2k+2) are the top bits of unit byte 4k+q
-            const uint32_t top = ((d[3 * u] >> 6) & 0x03030303u) | ((d[3 * u + 1] >> 4) & 0x0C0C0C0Cu) |
-                                 ((d[3 * u + 2] >> 2) & 0x30303030u);
+            // pair 12+q of the unit: bits [2k, 2k+2) are the top bits of unit
+            // byte 4k+q.  Byte q of `top` gets them at bits 2k..2k+1 by two
+            // bit-field inserts; its bits 6-7 keep other bits, which the table's
+            // copies over the top two index bits ignore.
+            const uint32_t t01 = bit_insert(0x03030303u, d[3 * u] >> 6, d[3 * u + 1] >> 4);
+            const uint32_t top = bit_insert(0x0F0F0F0Fu, t01, d[3 * u + 2] >> 2);
             return __builtin_amdgcn_perm(top, lane4, addr_sel<pu - 12>());
         }
     }
@@ -475,59 +487,40 @@ __device__ __forceinline__ float row_bcast31(float v)
 // next one (lane = row of the tile).  x from LDS (XL: staged [B][cols] fp16
 // at xl) or global memory.  acc[b * NC] is batch column b's first chain.
 //
-// The chunk's rows are non-decreasing, so their products form contiguous
-// segments.  Each row that starts inside the chunk marks its first lane
-// (a forward lane permute), a ballot turns the marks into a wave-wide mask,
-// and every lane's segment start is the mask's highest bit at or below it.
-// A segmented inclusive scan (DPP row shifts, then row broadcasts) sums each
-// segment up to every lane, and each row lane fetches the value at its last
-// nonzero in the chunk.
+// The chunk's rows are non-decreasing, so each row's products are a run of
+// lanes.  An inclusive prefix sum over the wave (DPP row shifts, then row
+// broadcasts) gives every run's sum as the difference of two prefix values,
+// which each row lane fetches from the run's last lane and the lane before
+// its first.
 template <int B, int NC, bool XL>
 __device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int cb, int v1, const KernelArgs &a, int lane,
                                              int rp_lo, int rp_hi, const uint16_t *xl, float *acc)
 {
-    const int i = cb + lane;
-    const int s_r = rp_lo - cb; // chunk lane of this row's first nonzero
-    const bool starts = rp_lo < rp_hi && s_r > 0 && s_r < 64;
-    const int mark = __builtin_amdgcn_ds_permute((starts ? s_r : 0) << 2, 1); // rows without a start mark lane 0
-    const uint64_t starts_mask = __builtin_amdgcn_ballot_w64(mark != 0) | 1ull;
-    const uint64_t upto = starts_mask & (~0ull >> (63 - lane));
-    const int seg0 = 63 - (int)__builtin_clzll(upto); // first lane of this nonzero's segment
-    const float vv = i < v1 ? f16_to_f32((uint16_t)valv) : 0.f;
+    const float vv = cb + lane < v1 ? f16_to_f32((uint16_t)valv) : 0.f;
     const int col = (int)colv;
-    float prod[B];
+    float pre[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const int64_t xi = (int64_t)b * a.cols + col;
-        prod[b] = vv * f16_to_f32(XL ? xl[xi] : a.x[xi]);
+        float v = vv * f16_to_f32(XL ? xl[xi] : a.x[xi]);
+        v += row_shr<1>(v);
+        v += row_shr<2>(v);
+        v += row_shr<4>(v);
+        v += row_shr<8>(v);
+        v += row_bcast15(v); // rows 1 and 3 (0 elsewhere)
+        v += row_bcast31(v); // rows 2 and 3 (0 elsewhere)
+        pre[b] = v;
     }
-    const int row_first = lane & ~15;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float v = prod[b];
-        float u = row_shr<1>(v);
-        if (lane - 1 >= seg0) v += u;
-        u = row_shr<2>(v);
-        if (lane - 2 >= seg0) v += u;
-        u = row_shr<4>(v);
-        if (lane - 4 >= seg0) v += u;
-        u = row_shr<8>(v);
-        if (lane - 8 >= seg0) v += u;
-        u = row_bcast15(v);
-        if (seg0 < row_first) v += u; // rows 1 and 3 (u is 0 in rows 0 and 2)
-        u = row_bcast31(v);
-        if (seg0 < 32) v += u; // rows 2 and 3 (u is 0 in rows 0 and 1)
-        prod[b] = v;
-    }
-    // lane r: the sum of row r's nonzeros in this chunk sits at the chunk lane
-    // of its last one
+    // lane r: row r's nonzeros in this chunk are chunk lanes [first, last]
     const int hi = min(min(rp_hi, cb + 64), v1);
-    const bool present = max(rp_lo, cb) < hi;
-    const int e = present ? hi - 1 - cb : 0;
+    const int first = max(rp_lo, cb) - cb, last = hi - 1 - cb;
+    const bool present = first <= last;
+    const int e_hi = present ? last : 0, e_lo = present && first > 0 ? first - 1 : 0;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const float got = lane_read(e, prod[b]);
-        if (present) acc[b * NC] += got;
+        const float top = lane_read(e_hi, pre[b]);
+        const float below = lane_read(e_lo, pre[b]);
+        if (present) acc[b * NC] += first > 0 ? top - below : top;
     }
 }
 
@@ -542,10 +535,10 @@ constexpr int kStageQuads = 4;
 
 // Round and store (or hand over) this workgroup's fp32 row sums.
 template <int B, bool ADDY>
-__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane, const float *tot)
+__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane, const float *tot, int count)
 {
     const int row = t * 64 + lane;
-    if (a.split == 1) {
+    if (count == 1) {
         if (row < a.rows) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
@@ -571,7 +564,7 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
             if (got == expected) break;
             expected = got;
         }
-        if ((int)(desired >> 32) == a.split) {
+        if ((int)(desired >> 32) == count) {
             if (row < a.rows) {
                 float v = __uint_as_float((uint32_t)desired);
                 if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.rows + row]);
@@ -797,7 +790,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         for (int k = 0; k < W; ++k) v += red[(k * B + b) * 64 + lane];
         tot[b] = v;
     }
-    finish_rows<B, ADDY>(a, t, lane, tot);
+    finish_rows<B, ADDY>(a, t, lane, tot, a.split);
 }
 
 template <int BITS, int B, int MODE>

@@ -466,3 +466,4 @@ def test_group_workload_levels(density_bp):
             y_ref, scale = oracle.dense_sparse_gemv(m.codes[sel], m.lut, 3, m.row_ptr, m.col, m.val, m.x,
                                                     rows=m.spec.rows, sel=sel)
             assert_close(y[:, torch.from_numpy(sel).cuda()], y_ref, scale, TOL, f"group {m.spec.name}")
+
