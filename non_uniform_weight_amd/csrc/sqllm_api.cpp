@@ -345,12 +345,11 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
             choose_split(a, total_tiles);
             if (a.split > 1 && (!workspace || workspace_bytes < ws_off)) return SQLLM_ERR_WORKSPACE;
             g.item[g.n] = a;
-            g.first[g.n] = (int)wgs;
+            if ((int64_t)a.tiles * a.split > g.wgs) g.wgs = a.tiles * a.split;
             wgs += (int64_t)a.tiles * a.split;
             ++g.n;
         }
         if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
-        g.first[g.n] = (int)wgs;
         LaunchShape ls{};
         ls.waves = choose_waves(wgs);
         for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);

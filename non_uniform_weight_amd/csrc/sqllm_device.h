@@ -590,9 +590,19 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
 // the first ring of code loads, then the first round of nonzeros.  Every dense step issues one group of loads
 // (placeholders past the wave's last group), so the wait before each group's
 // math lets exactly D-1 groups stay in flight.
+// Every argument (and the workgroup size) into registers at once: one round
+// of scalar loads at the start instead of one per first use.
+__device__ __forceinline__ void load_args_now(const KernelArgs &a)
+{
+    asm volatile("" ::"s"(a.packed), "s"(a.lut), "s"(a.row_ptr), "s"(a.col), "s"(a.val), "s"(a.x), "s"(a.y),
+                 "s"(a.slots), "s"(a.rows), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
+                 "s"(a.x_lds), "s"(blockDim.x));
+}
+
 template <int BITS, int B, int MODE>
 __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 {
+    load_args_now(a);
     constexpr bool DENSE = MODE != kSparseAdd;
     constexpr bool SPARSE = MODE != kDenseOnly;
     constexpr bool ADDY = MODE == kSparseAdd;
@@ -799,19 +809,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
     product_body<BITS, B, MODE>(a, blockIdx.x);
 }
 
-// Several independent products in one launch: workgroups [first[i],
-// first[i+1]) run product i.  The hardware starts a workgroup as soon as a
-// compute unit has room, so one product's start-up (table loads) and tail
-// (reductions) overlap the other products' code streams.
+// Several independent products in one launch: the workgroups of row y of the
+// grid run product y (those past its tiles x split workgroups exit at once).
+// The hardware starts workgroups in grid order as soon as a compute unit has
+// room, so one product's start-up (table rows, first code latency) and tail
+// (reductions) overlap the other products' code streams.  The product index
+// is blockIdx.y, so its arguments come in one round of scalar loads.
 template <int BITS, int B, int MODE>
 __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(GroupArgs g)
 {
-    const int bid = blockIdx.x;
-    int i = 0;
-#pragma unroll
-    for (int k = 1; k < kMaxGroup; ++k)
-        if (k < g.n && bid >= g.first[k]) i = k;
-    product_body<BITS, B, MODE>(g.item[i], bid - g.first[i]);
+    const KernelArgs &a = g.item[blockIdx.y];
+    load_args_now(a);
+    if ((int)blockIdx.x >= a.tiles * a.split) return;
+    product_body<BITS, B, MODE>(a, blockIdx.x);
 }
 
 template <int BITS, int B, int MODE>
@@ -844,7 +854,7 @@ hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream
         attr_set = true;
     }
     if (ls.waves < 1 || ls.waves > kMaxWaves || g.n < 1 || g.n > kMaxGroup) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)g.first[g.n]), block((unsigned)(64 * ls.waves));
+    const dim3 grid((unsigned)g.wgs, (unsigned)g.n), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, g);
     return hipGetLastError();
 }

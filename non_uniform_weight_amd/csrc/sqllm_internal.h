@@ -39,8 +39,8 @@ struct KernelArgs {
 // Independent products run by one launch (same bits and batch).
 constexpr int kMaxGroup = 8;
 struct GroupArgs {
-    int n;                        // products
-    int first[kMaxGroup + 1];     // first workgroup of product i; first[n] = grid size
+    int n;                        // products (grid rows)
+    int wgs;                      // grid columns: the most workgroups of any product
     KernelArgs item[kMaxGroup];
 };
 
