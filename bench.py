@@ -55,6 +55,10 @@ def parse():
                    help="level: one group launch per (q,k,v), (o), (gate,up), (down); single: one call per product")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
+    p.add_argument("--ablation", choices=("outliers",), default=None,
+                   help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
+                        "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
+                        "(one JSON line of its own)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
     return p.parse_args()
@@ -223,8 +227,89 @@ def cpu_baseline(stream_specs, seed: int, threads: int):
                       f"fp64 oracle incl. the |W||x| normaliser, {elapsed:.1f} s"}
 
 
+def outlier_ablation(args) -> None:
+    """Outlier cost over the dense-only product (summary page, Appendix C,
+    Table C.1 measures the same for its kernels): per product of the 13B
+    layer (Zipf-skewed rows) and the three 65B shapes (uniform rows), batch 1,
+    graph-timed launches cycling over copies of the inputs (>= 1.2 GB, so
+    nothing stays cached)."""
+    import numpy as np
+    import torch
+
+    import non_uniform_weight_amd as nw
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    modes = ("dense_only", "balanced", "one_thread_per_row", "stream_ordered")
+    rows_out = []
+    for wl, specs in ((3, synth.workload(3)), (4, synth.workload(4, batch=1))):
+        for i, spec in enumerate(specs):
+            m = synth.make_matrix(spec, seed=args.seed, workload=wl, index=i)
+            packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
+            reps = max(1, -(-1200 * 2 ** 20 // packed.numel()))
+            copies = []
+            for r in range(reps):
+                copies.append(dict(
+                    packed=packed if r == 0 else packed.clone(),
+                    lut=torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16),
+                    row_ptr=torch.from_numpy(m.row_ptr).cuda(), col=torch.from_numpy(m.col.view(np.int16)).cuda(),
+                    val=torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16)))
+            x = torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16)
+            y = torch.empty((1, spec.rows), dtype=torch.float16, device="cuda")
+            ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, 1), 256), dtype=torch.uint8,
+                             device="cuda")
+            res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "nnz": int(m.col.size)}
+            for mode in modes:
+                def call(c):
+                    if mode == "dense_only":
+                        nw.gemv(c["packed"], c["lut"], spec.bits, x, y=y, ws=ws, stream=stream)
+                    elif mode == "stream_ordered":
+                        nw.gemv(c["packed"], c["lut"], spec.bits, x, y=y, ws=ws, stream=stream)
+                        nw.spmv_add(c["row_ptr"], c["col"], c["val"], x, y, ws=ws, stream=stream)
+                    else:
+                        nw.dense_sparse_gemv(c["packed"], c["lut"], spec.bits, c["row_ptr"], c["col"], c["val"], x,
+                                             y=y, ws=ws, stream=stream)
+                nw.set_tuning(sparse_naive=1 if mode == "one_thread_per_row" else 0)
+                try:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        for k in range(20):
+                            call(copies[k % reps])
+                    with torch.cuda.stream(stream):
+                        for _ in range(5):
+                            g.replay()
+                        torch.cuda.synchronize()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(10):
+                            g.replay()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                finally:
+                    nw.set_tuning()
+                res[mode + "_us"] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+            for mode in modes[1:]:
+                res[mode + "_overhead_pct"] = round(100 * (res[mode + "_us"] / res["dense_only_us"] - 1), 1)
+            log(f"ablation {res}")
+            rows_out.append(res)
+            del copies, packed
+            torch.cuda.empty_cache()
+    summary = {}
+    for wl in (3, 4):
+        sel = [r for r in rows_out if r["workload"] == wl]
+        base = sum(r["dense_only_us"] for r in sel)
+        summary[f"workload{wl}"] = {mode: round(100 * (sum(r[mode + "_us"] for r in sel) / base - 1), 1)
+                                    for mode in modes[1:]}
+    print(json.dumps({"ablation": "outliers", "unit": "us per product, overhead % over dense-only",
+                      "batch": 1, "products": rows_out, "overhead_pct_total": summary}), flush=True)
+
+
 def main():
     args = parse()
+    if args.ablation == "outliers":
+        outlier_ablation(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the design notes describe row sharding across GPUs).", file=sys.stderr)

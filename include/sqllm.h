@@ -219,11 +219,14 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
  *   workgroup count the column split aims for, the fewest 256-column groups
  *   per workgroup, a forced split (1..64) and forced waves per workgroup
  *   (1..16).  0 restores a value's default (environment SQLLM_TARGET_WGS,
- *   SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES, else built in).  Shapes that no
+ *   SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES, else built in).  sparse_naive
+ *   = 1 switches the outliers to the unbalanced form for the ablation of the
+ *   balanced kernel (summary page, Appendix C, Table C.1): one thread per
+ *   row walks the row's nonzeros; 0 restores the balanced form.  Shapes that no
  *   compiled kernel fits fail with SQLLM_ERR_SHAPE.  Results agree within the
  *   stated tolerance for every shape; not thread-safe against concurrent
  *   calls. */
-sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves);
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive);
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
                                uint16_t *w, hipStream_t stream);
 

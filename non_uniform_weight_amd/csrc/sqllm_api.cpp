@@ -21,6 +21,7 @@ struct Tuning {
     int min_gps = 8;        // fewest column groups per workgroup (pair-table build amortisation)
     int force_split = 0;    // 0: choose; else workgroups per row tile
     int force_waves = 0;    // 0: choose; else waves per workgroup
+    int sparse_naive = 0;   // ablation: 1 = outliers one lane per row, unbalanced
     Tuning()
     {
         auto get = [](const char *name, int lo, int hi, int dflt) {
@@ -176,6 +177,7 @@ KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y,
     a.cols = (int)cols;
     a.tiles = (int)tiles_of(rows);
     a.groups = (int)(cols / kGroupCols);
+    a.sparse_naive = tuning().sparse_naive;
     return a;
 }
 
@@ -359,15 +361,16 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
     return SQLLM_OK;
 }
 
-sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves)
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive)
 {
     const Tuning dflt;
-    if (split > kMaxSplit || waves > kMaxWaves) return SQLLM_ERR_SHAPE;
+    if (split > kMaxSplit || waves > kMaxWaves || sparse_naive < 0 || sparse_naive > 1) return SQLLM_ERR_SHAPE;
     Tuning &t = tuning_state();
     t.target_wgs = target_wgs > 0 ? target_wgs : dflt.target_wgs;
     t.min_gps = min_gps > 0 ? min_gps : dflt.min_gps;
     t.force_split = split > 0 ? split : dflt.force_split;
     t.force_waves = waves > 0 ? waves : dflt.force_waves;
+    t.sparse_naive = sparse_naive;
     return SQLLM_OK;
 }
 

@@ -596,7 +596,7 @@ __device__ __forceinline__ void load_args_now(const KernelArgs &a)
 {
     asm volatile("" ::"s"(a.packed), "s"(a.lut), "s"(a.row_ptr), "s"(a.col), "s"(a.val), "s"(a.x), "s"(a.y),
                  "s"(a.slots), "s"(a.rows), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
-                 "s"(a.x_lds), "s"(blockDim.x));
+                 "s"(a.x_lds), "s"(a.sparse_naive), "s"(blockDim.x));
 }
 
 template <int BITS, int B, int MODE>
@@ -687,6 +687,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         const uint32_t per = len / parts, extra = len - per * parts;
         v0 = nz0 + (int)(part * per + min(part, extra));
         v1 = v0 + (int)(per + (part < extra ? 1u : 0u));
+        if (a.sparse_naive) v1 = v0; // the naive form below takes every nonzero
         sparse_round_load(cv, a, v0, v1, lane);
     }
 
@@ -763,6 +764,19 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 
     // -- 7. the rest of the nonzeros
     if constexpr (SPARSE) {
+        // the ablation's naive form (one thread per row, as an unbalanced CSR
+        // kernel does): wave 0 of the tile's first workgroup, lane = row
+        if (a.sparse_naive && s == 0 && w == 0) {
+            for (int i = rp_lo; i < rp_hi; ++i) {
+                const float vv = f16_to_f32(a.val[i]);
+                const int col = a.col[i];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int64_t xi = (int64_t)b * a.cols + col;
+                    acc[b * NC] += vv * f16_to_f32(a.x_lds ? xl[xi] : a.x[xi]);
+                }
+            }
+        }
         [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
             ((Ks >= done ? chunk(std::integral_constant<int, Ks>{}) : void()), ...);
         }(std::make_integer_sequence<int, R>{});

@@ -34,6 +34,7 @@ struct KernelArgs {
     int split;                // workgroups per row tile
     int gps;                  // column groups per workgroup (the last one may have fewer)
     int x_lds;                // 1: all of x staged in LDS for the outlier gathers
+    int sparse_naive;         // 1 (ablation): one lane per row walks its own nonzeros, no balancing
 };
 
 // Independent products run by one launch (same bits and batch).

@@ -163,9 +163,10 @@ def test_group_workspace_bytes(lib, nwpkg):
 
 
 def test_tuning_hook_bounds(lib):
-    assert lib.sqllm_test_tuning(0, 0, 65, 0) == 3      # split above 64
-    assert lib.sqllm_test_tuning(0, 0, 0, 17) == 3      # more than 16 waves
-    assert lib.sqllm_test_tuning(0, 0, 0, 0) == 0
+    assert lib.sqllm_test_tuning(0, 0, 65, 0, 0) == 3      # split above 64
+    assert lib.sqllm_test_tuning(0, 0, 0, 17, 0) == 3      # more than 16 waves
+    assert lib.sqllm_test_tuning(0, 0, 0, 0, 2) == 3       # outlier form 0 or 1
+    assert lib.sqllm_test_tuning(0, 0, 0, 0, 0) == 0
 
 
 def test_binding_refuses_host_tensors(nwpkg):

@@ -467,3 +467,39 @@ def test_group_workload_levels(density_bp):
                                                     rows=m.spec.rows, sel=sel)
             assert_close(y[:, torch.from_numpy(sel).cuda()], y_ref, scale, TOL, f"group {m.spec.name}")
 
+
+
+# ------------------------------------------------------------ outlier ablation
+
+@pytest.mark.parametrize("batch", [1, 3])
+@pytest.mark.parametrize("sparsity", ["5pct", "dense_row", "empty_rows"])
+def test_unbalanced_outlier_form_matches_oracle(batch, sparsity):
+    """The ablation's one-thread-per-row outlier form gives the same product
+    (within tolerance) as the balanced form, fused and outlier-only."""
+    rng = np.random.default_rng(stable_seed("naive", batch, sparsity))
+    codes, lut, x, rp, col, val = _make_case(rng, 193, 4096, 3, batch, sparsity)
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+    d = DevMatrix(codes, lut, 3, rp, col, val, x)
+    try:
+        nw().set_tuning(sparse_naive=1)
+        step(f"unbalanced outliers batch {batch} {sparsity}")
+        y = d.fused()
+        ys = d.spmv_add(d.gemv())
+        torch.cuda.synchronize()
+    finally:
+        nw().set_tuning()
+    assert_close(y, y_ref, scale, TOL, "fused, unbalanced outliers")
+    assert_close(ys, y_ref, scale, TOL, "stream-ordered, unbalanced outliers")
+
+
+def test_unbalanced_outlier_form_skewed_workload_rows():
+    """The 13B layer's Zipf-skewed down projection (rows holding every
+    column), sampled rows, unbalanced form."""
+    spec = synth.workload(3)[6]
+    m = synth.make_matrix(spec, seed=0, workload=3, index=6)
+    try:
+        nw().set_tuning(sparse_naive=1)
+        step(f"unbalanced outliers {spec}")
+        _check_matrix(m, np.arange(0, spec.rows, 7))
+    finally:
+        nw().set_tuning()
