@@ -1,0 +1,107 @@
+"""Pins of the offline oracle (oracle/quantize.py) against facts fixed by the
+pages and by the mathematics, not by retyping its code (CPU only).
+
+  - thresholds of a matrix whose sorted order is known by construction;
+  - W = D + S exactly, CSR in row order, D zero where S has entries;
+  - k-means: data equal to the starting centroids stays put with zero error;
+    uniform data converges to the optimal uniform quantizer's centres
+    (2j+1)/(2k); the objective never increases from step to step; a
+    centroid's cluster dominated by one heavily weighted value moves onto it
+    (Eq. 6); the k-means table beats a uniform grid on heavy-tailed rows.
+"""
+import numpy as np
+import pytest
+
+from oracle import quantize as q
+from seeds import stable_seed
+
+
+def f16(v):
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def test_thresholds_of_a_known_order():
+    rng = np.random.default_rng(stable_seed("thr"))
+    vals = np.unique(rng.normal(0, 1, 5000).astype(np.float16))  # distinct fp16 values, ascending
+    n = vals.size
+    mat = rng.permutation(vals).view(np.uint16).reshape(1, n)
+    for ppm in (2000, 50000, 0):
+        t_min, t_max, nnz = q.thresholds(mat, ppm)
+        n_tail = n * ppm // 1_000_000
+        assert t_min == int(vals.view(np.uint16)[n_tail])
+        assert t_max == int(vals.view(np.uint16)[n - 1 - n_tail])
+        assert nnz == 2 * n_tail  # distinct values: exactly n_tail below and above
+
+
+def test_thresholds_signed_zero_order():
+    # -0 sorts before +0; both compare equal as numbers, so neither is an outlier
+    mat = np.array([[0x8000, 0x0000, 0x3C00, 0xBC00]], dtype=np.uint16)  # -0, +0, 1, -1
+    t_min, t_max, nnz = q.thresholds(mat, 250000)  # one value per tail
+    assert (t_min, t_max) == (0x8000, 0x0000)
+    assert nnz == 2  # -1 and 1
+
+
+def test_extract_reconstructs_w():
+    rng = np.random.default_rng(stable_seed("extract"))
+    w = f16(rng.standard_t(3, (37, 300)) * 0.02).reshape(37, 300)
+    t_min, t_max, nnz = q.thresholds(w, 20000)
+    rp, col, val, dense = q.extract(w, t_min, t_max)
+    assert rp[0] == 0 and rp[-1] == nnz == col.size == val.size
+    assert np.all(np.diff(rp) >= 0)
+    s = np.zeros(w.shape, dtype=np.float64)
+    for r in range(w.shape[0]):
+        cs = col[rp[r]:rp[r + 1]].astype(np.int64)
+        assert np.all(np.diff(cs) > 0)
+        s[r, cs] = q.f16_to_f64(val[rp[r]:rp[r + 1]])
+    d = q.f16_to_f64(dense)
+    assert np.array_equal(d + s, q.f16_to_f64(w))
+    assert np.all(d[s != 0] == 0)
+    lo, hi = q.f16_to_f64(np.array([t_min, t_max]))
+    assert np.all((d >= lo) & (d <= hi) | (d == 0))
+
+
+def test_kmeans_keeps_data_that_equals_the_start():
+    x = np.repeat(np.arange(8, dtype=np.float64), 5)
+    c = q.kmeans_row(x, None, 8, 10)
+    assert np.array_equal(c, np.arange(8, dtype=np.float64))
+    codes, lut = q.kmeans_lut(f16(x).reshape(1, -1), None, 3, 10)
+    assert np.all(q.objective(f16(x).reshape(1, -1), None, codes, lut) == 0)
+
+
+@pytest.mark.parametrize("k", [8, 16])
+def test_kmeans_uniform_data_reaches_optimal_uniform_quantizer(k):
+    x = (np.arange(20000) + 0.5) / 20000  # uniform on [0, 1]
+    c = q.kmeans_row(x, None, k, 400)
+    assert np.allclose(c, (2 * np.arange(k) + 1) / (2 * k), atol=2e-3)
+
+
+def test_kmeans_objective_never_increases():
+    rng = np.random.default_rng(stable_seed("mono"))
+    x = rng.standard_t(4, 3000) * 0.02
+    wt = rng.exponential(1.0, 3000)
+    prev = np.inf
+    for it in range(12):
+        c = q.kmeans_row(x, wt, 8, it)
+        obj = (wt * (x - c[q.nearest(x, c)]) ** 2).sum()
+        assert obj <= prev * (1 + 1e-12)
+        prev = obj
+
+
+def test_weighted_centroid_moves_onto_dominant_value():
+    x = np.array([0.0, 0.1, 0.2, 10.0, 10.5, 11.0])
+    wt = np.array([1.0, 1e9, 1.0, 1.0, 1.0, 1.0])
+    c = q.kmeans_row(x, wt, 2, 20)
+    assert abs(c[0] - 0.1) < 1e-6
+    assert abs(c[1] - 10.5) < 1e-12
+
+
+def test_kmeans_beats_uniform_grid_on_heavy_tails():
+    rng = np.random.default_rng(stable_seed("rtn"))
+    w = f16(rng.standard_t(3, (8, 2048)) * 0.02).reshape(8, 2048)
+    codes, lut = q.kmeans_lut(w, None, 3, 20)
+    err_km = q.objective(w, None, codes, lut)
+    x = q.f16_to_f64(w)
+    for r in range(8):
+        grid = np.linspace(x[r].min(), x[r].max(), 8)
+        err_u = ((x[r] - grid[q.nearest(x[r], grid)]) ** 2).sum()
+        assert err_km[r] < err_u
