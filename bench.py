@@ -55,10 +55,10 @@ def parse():
                    help="level: one group launch per (q,k,v), (o), (gate,up), (down); single: one call per product")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
-    p.add_argument("--ablation", choices=("outliers",), default=None,
+    p.add_argument("--ablation", choices=("outliers", "batch"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
-                        "(one JSON line of its own)")
+                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
     return p.parse_args()
@@ -305,10 +305,69 @@ def outlier_ablation(args) -> None:
                       "batch": 1, "products": rows_out, "overhead_pct_total": summary}), flush=True)
 
 
+def batch_ablation(args) -> None:
+    """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4 and 8:
+    µs per product and effective GB/s (bytes grow only by x and y, the math by
+    the batch), graph-timed over copies of the inputs (>= 1.2 GB)."""
+    import numpy as np
+    import torch
+
+    import non_uniform_weight_amd as nw
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    out = []
+    for batch in (1, 2, 4, 8):
+        for i, spec in enumerate(synth.workload(4, batch=batch)):
+            m = synth.make_matrix(spec, seed=args.seed, workload=4, index=i)
+            packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
+            lut = torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16)
+            rp = torch.from_numpy(m.row_ptr).cuda()
+            col = torch.from_numpy(m.col.view(np.int16)).cuda()
+            val = torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16)
+            x = torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16)
+            reps = max(1, -(-1200 * 2 ** 20 // packed.numel()))
+            # every copy holds its own codes, tables and CSR: nothing but x stays cache-resident
+            copies = [(packed, lut, rp, col, val)] + [tuple(t.clone() for t in (packed, lut, rp, col, val))
+                                                      for _ in range(reps - 1)]
+            y = torch.empty((batch, spec.rows), dtype=torch.float16, device="cuda")
+            ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, batch), 256), dtype=torch.uint8,
+                             device="cuda")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for k in range(20):
+                    c = copies[k % reps]
+                    nw.dense_sparse_gemv(c[0], c[1], spec.bits, c[2], c[3], c[4], x, y=y, ws=ws, stream=stream)
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(10):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 200 * 1e3
+            nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, int(m.col.size), batch)
+            res = {"batch": batch, "shape": f"{spec.rows}x{spec.cols}", "us": round(us, 3),
+                   "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            log(f"batch ablation {res}")
+            out.append(res)
+            del copies, packed, lut, rp, col, val
+            torch.cuda.empty_cache()
+    print(json.dumps({"ablation": "batch", "unit": "us per product and effective GB/s", "products": out}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.ablation == "outliers":
         outlier_ablation(args)
+        return
+    if args.ablation == "batch":
+        batch_ablation(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
