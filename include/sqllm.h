@@ -102,7 +102,8 @@ typedef enum {
     SQLLM_ERR_ALIGN = 5,      /* a pointer is not aligned as required */
     SQLLM_ERR_CODE_RANGE = 6, /* sqllm_pack: a code is >= 2^bits */
     SQLLM_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed */
-    SQLLM_ERR_WORKSPACE = 8   /* workspace missing, misaligned or too small */
+    SQLLM_ERR_WORKSPACE = 8,  /* workspace missing, misaligned or too small */
+    SQLLM_ERR_CAPACITY = 9    /* sqllm_outlier_extract: more outliers than the CSR buffers hold */
 } sqllm_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -205,6 +206,60 @@ size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch)
 
 sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, int bits, int batch, void *workspace,
                                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Offline steps upstream of the product (not timed on the hot path): the
+ * dense-and-sparse split of an fp16 weight matrix W and the per-row
+ * (optionally sensitivity-weighted) k-means that yields the codes and the
+ * tables.  SqueezeLLM: Dense-and-Sparse Quantization, summary page, §3.4
+ * "The Dense-and-Sparse Decomposition" (W = D + S, S the weights outside
+ * the [T_min, T_max] percentile range, in CSR) and §3.3, Eq. 1 / Eq. 6 with
+ * "The weighted k-means algorithm in practice" (per output channel: assign
+ * each weight to the nearest centroid, move each centroid to the
+ * sensitivity-weighted mean of its weights).  Device pointers owned by the
+ * caller; W is fp16 [rows][cols] row-major, 1 <= cols <= 65536 and
+ * rows * cols <= 2^31 - 1 (else SQLLM_ERR_SHAPE, and workspace bytes 0).
+ *
+ * sqllm_quantize_workspace_bytes: device scratch the two split calls need.
+ */
+size_t sqllm_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * sqllm_outlier_thresholds: T_min and T_max of W at tail_ppm parts per
+ * million on each side (2000 = the pages' 0.2 / 99.8 percentiles): the
+ * values of rank floor(rows * cols * tail_ppm / 1e6) from the low and the
+ * high end of W's fp16 values ordered as IEEE total order (-0 before +0);
+ * and *nnz, the number of weights comparing below T_min or above T_max.
+ * 0 <= tail_ppm < 500000.  t_min, t_max (fp16 bits) and nnz are HOST
+ * outputs; the call synchronises `stream`.
+ */
+sqllm_status sqllm_outlier_thresholds(const uint16_t *w, int64_t rows, int64_t cols, int tail_ppm, void *workspace,
+                                      size_t workspace_bytes, uint16_t *t_min, uint16_t *t_max, int64_t *nnz,
+                                      hipStream_t stream);
+
+/*
+ * sqllm_outlier_extract: S = the weights below t_min or above t_max as CSR
+ * (row_ptr int32 [rows + 1]; col_idx uint16 and val fp16 [nnz], columns
+ * ascending within a row) and D = W with zeros at S's entries (fp16
+ * [rows][cols], must not overlap W).  Writes past nnz_capacity are dropped
+ * and reported as SQLLM_ERR_CAPACITY; the call synchronises `stream`.
+ */
+sqllm_status sqllm_outlier_extract(const uint16_t *w, int64_t rows, int64_t cols, uint16_t t_min, uint16_t t_max,
+                                   int32_t *row_ptr, uint16_t *col_idx, uint16_t *val, int64_t nnz_capacity,
+                                   uint16_t *dense, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sqllm_kmeans_lut: per row of D, 2^bits centroids by `iters` k-means steps
+ * from uniformly spaced starts over the row's range (each weight to the
+ * nearest centroid, ties to the lower; each centroid to the weighted mean
+ * of its weights, unchanged when it has none; sens = NULL weighs all
+ * equally, else fp32 [rows][cols] non-negative sensitivities), then the
+ * centroids rounded to fp16 into lut [rows][2^bits] and every weight's code
+ * (uint8 [rows][cols]) = its nearest fp16 centroid, ties to the lower.
+ * Asynchronous on `stream`; 0 <= iters <= 1000.
+ */
+sqllm_status sqllm_kmeans_lut(const uint16_t *dense, const float *sens, int64_t rows, int64_t cols, int bits, int iters,
+                              uint8_t *codes, uint16_t *lut, hipStream_t stream);
 
 /*
  * Test-only exports (not part of the stable contract).  The readers are

@@ -55,6 +55,16 @@ _lib.sqllm_group_workspace_bytes.restype = _sz
 _lib.sqllm_group_workspace_bytes.argtypes = [ctypes.POINTER(Product), _i32, _i32]
 _lib.sqllm_dense_sparse_gemv_group.restype = _i32
 _lib.sqllm_dense_sparse_gemv_group.argtypes = [ctypes.POINTER(Product), _i32, _i32, _i32, _vp, _sz, _vp]
+_lib.sqllm_quantize_workspace_bytes.restype = _sz
+_lib.sqllm_quantize_workspace_bytes.argtypes = [_i64, _i64]
+_lib.sqllm_outlier_thresholds.restype = _i32
+_lib.sqllm_outlier_thresholds.argtypes = [_vp, _i64, _i64, _i32, _vp, _sz, ctypes.POINTER(ctypes.c_uint16),
+                                          ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(_i64), _vp]
+_lib.sqllm_outlier_extract.restype = _i32
+_lib.sqllm_outlier_extract.argtypes = [_vp, _i64, _i64, ctypes.c_uint16, ctypes.c_uint16, _vp, _vp, _vp, _i64, _vp,
+                                       _vp, _sz, _vp]
+_lib.sqllm_kmeans_lut.restype = _i32
+_lib.sqllm_kmeans_lut.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]
 _lib.sqllm_test_unpack.restype = _i32
 _lib.sqllm_test_unpack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
 _lib.sqllm_test_tuning.restype = _i32
@@ -64,7 +74,8 @@ _lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
 
 EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes", "sqllm_pack", "sqllm_gemv",
            "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_group_workspace_bytes",
-           "sqllm_dense_sparse_gemv_group", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning")
+           "sqllm_dense_sparse_gemv_group", "sqllm_quantize_workspace_bytes", "sqllm_outlier_thresholds",
+           "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning")
 MAX_GROUP = 8
 
 SQLLM_OK = 0
@@ -234,6 +245,50 @@ def dense_sparse_gemv_group(items, bits: int, ws: torch.Tensor | None = None, st
         ws = _cached_workspace(need, items[0]["x"].device)
     _check(_lib.sqllm_dense_sparse_gemv_group(arr, len(items), bits, batch, _dev(ws, "workspace", torch.uint8),
                                               ws.numel(), _stream(stream)), "sqllm_dense_sparse_gemv_group")
+
+
+def _quantize_ws(rows: int, cols: int, device) -> torch.Tensor:
+    n = int(_lib.sqllm_quantize_workspace_bytes(rows, cols))
+    if n == 0:
+        raise ValueError(f"unsupported shape ({rows}, {cols})")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def outlier_thresholds(w: torch.Tensor, tail_ppm: int = 2000, stream=None):
+    """(T_min, T_max, nnz) of an fp16 [rows, cols] weight matrix (fp16 bit patterns as ints; synchronises)."""
+    rows, cols = w.shape
+    ws = _quantize_ws(rows, cols, w.device)
+    lo, hi, nnz = ctypes.c_uint16(), ctypes.c_uint16(), ctypes.c_int64()
+    _check(_lib.sqllm_outlier_thresholds(_dev(w, "w", torch.float16), rows, cols, tail_ppm, ws.data_ptr(), ws.numel(),
+                                         ctypes.byref(lo), ctypes.byref(hi), ctypes.byref(nnz), _stream(stream)),
+           "sqllm_outlier_thresholds")
+    return lo.value, hi.value, nnz.value
+
+
+def outlier_extract(w: torch.Tensor, t_min: int, t_max: int, nnz: int, stream=None):
+    """W = D + S: (row_ptr int32, col int16 bits, val fp16, dense fp16) (synchronises)."""
+    rows, cols = w.shape
+    ws = _quantize_ws(rows, cols, w.device)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=w.device)
+    col = torch.empty(max(nnz, 1), dtype=torch.int16, device=w.device)
+    val = torch.empty(max(nnz, 1), dtype=torch.float16, device=w.device)
+    dense = torch.empty_like(w)
+    _check(_lib.sqllm_outlier_extract(_dev(w, "w", torch.float16), rows, cols, t_min, t_max, row_ptr.data_ptr(),
+                                      col.data_ptr(), val.data_ptr(), nnz, _dev(dense, "dense", torch.float16),
+                                      ws.data_ptr(), ws.numel(), _stream(stream)), "sqllm_outlier_extract")
+    return row_ptr, col[:nnz], val[:nnz], dense
+
+
+def kmeans_lut(dense: torch.Tensor, bits: int, iters: int = 20, sens: torch.Tensor | None = None, stream=None):
+    """Per-row k-means codes (uint8 [rows, cols]) and fp16 tables [rows, 2^bits] of D."""
+    rows, cols = dense.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dense.device)
+    lut = torch.empty((rows, 1 << bits), dtype=torch.float16, device=dense.device)
+    sp = None if sens is None else _dev(sens, "sens", torch.float32)
+    _check(_lib.sqllm_kmeans_lut(_dev(dense, "dense", torch.float16), sp, rows, cols, bits, iters,
+                                 _dev(codes, "codes", torch.uint8), _dev(lut, "lut", torch.float16), _stream(stream)),
+           "sqllm_kmeans_lut")
+    return codes, lut
 
 
 def unpack_codes(packed, rows, cols, bits, stream=None) -> torch.Tensor:

@@ -197,6 +197,7 @@ const char *sqllm_status_string(sqllm_status s)
     case SQLLM_ERR_CODE_RANGE: return "SQLLM_ERR_CODE_RANGE: a code is >= 2^bits";
     case SQLLM_ERR_HIP: return "SQLLM_ERR_HIP: HIP runtime or launch failure";
     case SQLLM_ERR_WORKSPACE: return "SQLLM_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case SQLLM_ERR_CAPACITY: return "SQLLM_ERR_CAPACITY: more outliers than the CSR buffers hold";
     }
     return "SQLLM_ERR_UNKNOWN";
 }
@@ -358,6 +359,98 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
         if (launch_dense_sparse_group(g, bits, batch, fused ? kFused : kDenseOnly, ls, stream) != hipSuccess)
             return SQLLM_ERR_HIP;
     }
+    return SQLLM_OK;
+}
+
+// ---- offline split and k-means
+
+namespace {
+constexpr size_t kBinsBytes = 65536 * 4;
+constexpr size_t kMiscBytes = 256; // keys, total, overflow flag
+
+sqllm_status quantize_shape(const void *w, int64_t rows, int64_t cols)
+{
+    if (!w) return SQLLM_ERR_NULL;
+    if (rows < 1 || cols < 1 || cols > 65536 || rows > INT32_MAX / cols) return SQLLM_ERR_SHAPE;
+    if (!aligned(w, 2)) return SQLLM_ERR_ALIGN;
+    return SQLLM_OK;
+}
+} // namespace
+
+size_t sqllm_quantize_workspace_bytes(int64_t rows, int64_t cols)
+{
+    if (rows < 1 || cols < 1 || cols > 65536 || rows > INT32_MAX / cols) return 0;
+    return kBinsBytes + kMiscBytes + (size_t)rows * 4;
+}
+
+sqllm_status sqllm_outlier_thresholds(const uint16_t *w, int64_t rows, int64_t cols, int tail_ppm, void *workspace,
+                                      size_t workspace_bytes, uint16_t *t_min, uint16_t *t_max, int64_t *nnz,
+                                      hipStream_t stream)
+{
+    sqllm_status st = quantize_shape(w, rows, cols);
+    if (st != SQLLM_OK) return st;
+    if (!t_min || !t_max || !nnz) return SQLLM_ERR_NULL;
+    if (tail_ppm < 0 || tail_ppm >= 500000) return SQLLM_ERR_SHAPE;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < sqllm_quantize_workspace_bytes(rows, cols))
+        return SQLLM_ERR_WORKSPACE;
+    const int64_t n = rows * cols;
+    const int64_t tail = (n / 1000000) * tail_ppm + ((n % 1000000) * tail_ppm) / 1000000;
+    uint32_t *bins = (uint32_t *)workspace;
+    uint32_t *keys = (uint32_t *)((char *)workspace + kBinsBytes);
+    unsigned long long *total = (unsigned long long *)((char *)workspace + kBinsBytes + 64);
+    int32_t *counts = (int32_t *)((char *)workspace + kBinsBytes + kMiscBytes);
+    uint32_t hk[2] = {0, 0};
+    unsigned long long ht = 0;
+    if (launch_thresholds(w, n, tail, bins, keys, stream) != hipSuccess ||
+        hipMemcpyAsync(hk, keys, sizeof(hk), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
+    if (hipMemsetAsync(total, 0, sizeof(*total), stream) != hipSuccess ||
+        launch_outlier_count(w, (int)rows, (int)cols, (uint16_t)hk[0], (uint16_t)hk[1], counts, total, stream) !=
+            hipSuccess ||
+        hipMemcpyAsync(&ht, total, sizeof(ht), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
+    *t_min = (uint16_t)hk[0];
+    *t_max = (uint16_t)hk[1];
+    *nnz = (int64_t)ht;
+    return SQLLM_OK;
+}
+
+sqllm_status sqllm_outlier_extract(const uint16_t *w, int64_t rows, int64_t cols, uint16_t t_min, uint16_t t_max,
+                                   int32_t *row_ptr, uint16_t *col_idx, uint16_t *val, int64_t nnz_capacity,
+                                   uint16_t *dense, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    sqllm_status st = quantize_shape(w, rows, cols);
+    if (st != SQLLM_OK) return st;
+    if (!row_ptr || !dense || (nnz_capacity > 0 && (!col_idx || !val))) return SQLLM_ERR_NULL;
+    if (nnz_capacity < 0) return SQLLM_ERR_SHAPE;
+    if (!aligned(row_ptr, 4) || !aligned(dense, 2)) return SQLLM_ERR_ALIGN;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < sqllm_quantize_workspace_bytes(rows, cols))
+        return SQLLM_ERR_WORKSPACE;
+    int *overflow = (int *)((char *)workspace + kBinsBytes + 128);
+    int32_t *counts = (int32_t *)((char *)workspace + kBinsBytes + kMiscBytes);
+    int hov = 0;
+    if (hipMemsetAsync(overflow, 0, sizeof(int), stream) != hipSuccess ||
+        launch_outlier_extract(w, (int)rows, (int)cols, t_min, t_max, counts, row_ptr, col_idx, val, nnz_capacity,
+                               dense, overflow, stream) != hipSuccess ||
+        hipMemcpyAsync(&hov, overflow, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
+    return hov ? SQLLM_ERR_CAPACITY : SQLLM_OK;
+}
+
+sqllm_status sqllm_kmeans_lut(const uint16_t *dense, const float *sens, int64_t rows, int64_t cols, int bits, int iters,
+                              uint8_t *codes, uint16_t *lut, hipStream_t stream)
+{
+    sqllm_status st = quantize_shape(dense, rows, cols);
+    if (st != SQLLM_OK) return st;
+    if (!codes || !lut) return SQLLM_ERR_NULL;
+    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (iters < 0 || iters > 1000) return SQLLM_ERR_SHAPE;
+    if (!aligned(lut, 2) || (sens && !aligned(sens, 4))) return SQLLM_ERR_ALIGN;
+    if (launch_kmeans(dense, sens, (int)rows, (int)cols, bits, iters, codes, lut, stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }
 

@@ -55,6 +55,15 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
                                hipStream_t stream);
 hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mode mode, const LaunchShape &ls,
                                      hipStream_t stream);
+hipError_t launch_thresholds(const uint16_t *w, int64_t n, int64_t tail, uint32_t *bins, uint32_t *keys,
+                             hipStream_t stream);
+hipError_t launch_outlier_count(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
+                                int32_t *counts, unsigned long long *total, hipStream_t stream);
+hipError_t launch_outlier_extract(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
+                                  int32_t *counts, int32_t *row_ptr, uint16_t *col_idx, uint16_t *val,
+                                  int64_t capacity, uint16_t *dense, int *overflow, hipStream_t stream);
+hipError_t launch_kmeans(const uint16_t *dense, const float *sens, int rows, int cols, int bits, int iters,
+                         uint8_t *codes, uint16_t *lut, hipStream_t stream);
 hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void *packed, int *bad, hipStream_t stream);
 hipError_t launch_unpack(const void *packed, const uint16_t *lut, int rows, int cols, int bits, uint8_t *codes,
                          uint16_t *w, hipStream_t stream);

@@ -29,14 +29,14 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.sqllm_status_string(code).startswith(b"SQLLM_")
     assert lib.sqllm_status_string(99) == b"SQLLM_ERR_UNKNOWN"
 
@@ -167,6 +167,48 @@ def test_tuning_hook_bounds(lib):
     assert lib.sqllm_test_tuning(0, 0, 0, 17, 0) == 3      # more than 16 waves
     assert lib.sqllm_test_tuning(0, 0, 0, 0, 2) == 3       # outlier form 0 or 1
     assert lib.sqllm_test_tuning(0, 0, 0, 0, 0) == 0
+
+
+def test_quantize_argument_errors(lib):
+    u16 = ctypes.c_uint16
+    lo, hi, nnz = u16(), u16(), ctypes.c_int64()
+    ws = P(0x200000)
+    wsb = lib.sqllm_quantize_workspace_bytes(64, 256)
+    assert wsb == 65536 * 4 + 256 + 64 * 4
+    assert lib.sqllm_quantize_workspace_bytes(64, 65537) == 0
+    assert lib.sqllm_quantize_workspace_bytes(1 << 20, 4096) == 0       # more than 2^31 - 1 weights
+    assert lib.sqllm_quantize_workspace_bytes(0, 256) == 0
+
+    def thr(w=A16, rows=64, cols=256, ppm=2000, ws=ws, wsb=wsb, out=True):
+        refs = (ctypes.byref(lo), ctypes.byref(hi), ctypes.byref(nnz)) if out else (None, None, None)
+        return lib.sqllm_outlier_thresholds(w, rows, cols, ppm, ws, wsb, *refs, None)
+    assert thr(w=None) == 1
+    assert thr(out=False) == 1
+    assert thr(cols=65537) == 3
+    assert thr(ppm=500000) == 3
+    assert thr(ppm=-1) == 3
+    assert thr(w=P(0x100001)) == 5
+    assert thr(ws=None) == 8
+    assert thr(ws=P(0x200080)) == 8                                      # not 256-byte aligned
+    assert thr(wsb=wsb - 1) == 8
+
+    def ext(w=A16, rp=A16, cap=10, col=B16, dense=B16, ws=ws, wsb=wsb):
+        return lib.sqllm_outlier_extract(w, 64, 256, 0x8000, 0, rp, col, B16, cap, dense, ws, wsb, None)
+    assert ext(rp=None) == 1
+    assert ext(dense=None) == 1
+    assert ext(col=None) == 1
+    assert ext(cap=-1) == 3
+    assert ext(rp=P(0x100002)) == 5
+    assert ext(wsb=0) == 8
+
+    def km(d=A16, bits=3, iters=10, codes=B16, lut=B16, sens=None):
+        return lib.sqllm_kmeans_lut(d, sens, 64, 256, bits, iters, codes, lut, None)
+    assert km(d=None) == 1
+    assert km(codes=None) == 1
+    assert km(bits=2) == 2
+    assert km(iters=1001) == 3
+    assert km(lut=P(0x100001)) == 5
+    assert km(sens=P(0x100002)) == 5
 
 
 def test_binding_refuses_host_tensors(nwpkg):
