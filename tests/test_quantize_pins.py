@@ -105,3 +105,59 @@ def test_kmeans_beats_uniform_grid_on_heavy_tails():
         grid = np.linspace(x[r].min(), x[r].max(), 8)
         err_u = ((x[r] - grid[q.nearest(x[r], grid)]) ** 2).sum()
         assert err_km[r] < err_u
+
+
+def test_sensitive_threshold_of_a_known_order():
+    rng = np.random.default_rng(stable_seed("sens-thr"))
+    vals = np.unique(rng.exponential(1.0, 4000).astype(np.float32))  # distinct, ascending
+    n = vals.size
+    mat = rng.permutation(vals).reshape(4, n // 4) if n % 4 == 0 else rng.permutation(vals).reshape(1, n)
+    for ppm in (500, 50000, 0):
+        t_s = q.sensitive_threshold(mat, ppm)
+        n_top = n * ppm // 1_000_000
+        assert t_s == vals[n - 1 - n_top]
+        assert np.count_nonzero(mat > t_s) == n_top
+
+
+def test_split_with_sensitive_values_is_the_union():
+    """Planted outliers O (5 on each tail) and planted most-sensitive weights
+    P (3, one of them also an outlier): S is exactly O | P."""
+    rng = np.random.default_rng(stable_seed("union"))
+    rows, cols = 20, 100
+    w = rng.uniform(-0.01, 0.01, (rows, cols))
+    flat = rng.permutation(rows * cols)
+    o_pos, p_pos = flat[:10], np.concatenate([flat[:1], flat[10:12]])
+    w.ravel()[o_pos[:5]] = [1.0, 1.5, 2.0, 2.5, 3.0]
+    w.ravel()[o_pos[5:]] = [-1.0, -1.5, -2.0, -2.5, -3.0]
+    w_bits = f16(w).reshape(rows, cols)
+    sens = rng.uniform(0, 1, (rows, cols)).astype(np.float32)
+    sens.ravel()[p_pos] = [10.0, 11.0, 12.0]
+    t_min, t_max, t_s, nnz = q.split_thresholds(w_bits, 2500, sens, 1500)   # 5 per tail, top 3
+    want = set(o_pos.tolist()) | set(p_pos.tolist())
+    assert nnz == len(want) == 12
+    rp, col, val, dense = q.extract(w_bits, t_min, t_max, sens, t_s)
+    got = {int(r) * cols + int(c) for r in range(rows) for c in col[rp[r]:rp[r + 1]]}
+    assert got == want
+    s = np.zeros((rows, cols))
+    for r in range(rows):
+        s[r, col[rp[r]:rp[r + 1]].astype(np.int64)] = q.f16_to_f64(val[rp[r]:rp[r + 1]])
+    assert np.array_equal(q.f16_to_f64(dense) + s, q.f16_to_f64(w_bits))
+    ds = q.dense_sensitivity(sens, rp, col)
+    mask = np.zeros(rows * cols, bool)
+    mask[list(want)] = True
+    mask = mask.reshape(rows, cols)
+    assert np.all(ds[mask] == 0) and np.array_equal(ds[~mask], sens[~mask])
+
+
+def test_zero_sensitivity_weights_take_no_part():
+    """A weight of zero sensitivity moves no centroid: the same centroids as
+    clustering without it (its value inside the row's range)."""
+    rng = np.random.default_rng(stable_seed("zero-sens"))
+    x = rng.normal(0, 1, 3000)
+    wt = rng.exponential(1.0, 3000)
+    inner = np.flatnonzero((x > np.sort(x)[10]) & (x < np.sort(x)[-10]))[:200]
+    wt[inner] = 0
+    keep = wt > 0
+    c_all = q.kmeans_row(x, wt, 8, 15)
+    c_sub = q.kmeans_row(x[keep], wt[keep], 8, 15)
+    assert np.allclose(c_all, c_sub, rtol=1e-12, atol=0)
