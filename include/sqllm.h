@@ -216,7 +216,9 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
  * the [T_min, T_max] percentile range, in CSR) and §3.3, Eq. 1 / Eq. 6 with
  * "The weighted k-means algorithm in practice" (per output channel: assign
  * each weight to the nearest centroid, move each centroid to the
- * sensitivity-weighted mean of its weights).  Device pointers owned by the
+ * sensitivity-weighted mean of its weights); that subsection's paragraph
+ * on sensitive values adds the most sensitive weights (0.05%) to S.
+ * Device pointers owned by the
  * caller; W is fp16 [rows][cols] row-major, 1 <= cols <= 65536 and
  * rows * cols <= 2^31 - 1 (else SQLLM_ERR_SHAPE, and workspace bytes 0).
  *
@@ -228,25 +230,36 @@ size_t sqllm_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * sqllm_outlier_thresholds: T_min and T_max of W at tail_ppm parts per
  * million on each side (2000 = the pages' 0.2 / 99.8 percentiles): the
  * values of rank floor(rows * cols * tail_ppm / 1e6) from the low and the
- * high end of W's fp16 values ordered as IEEE total order (-0 before +0);
- * and *nnz, the number of weights comparing below T_min or above T_max.
- * 0 <= tail_ppm < 500000.  t_min, t_max (fp16 bits) and nnz are HOST
- * outputs; the call synchronises `stream`.
+ * high end of W's fp16 values ordered as IEEE total order (-0 before +0).
+ * Given sensitivities `sens` (fp32 [rows][cols], e.g. a Fisher diagonal;
+ * NULL for none), also T_s: with n_top = floor(rows * cols * top_ppm / 1e6),
+ * the sensitivity of rank rows * cols - 1 - n_top in ascending total order
+ * (500 = the pages' 0.05% most sensitive values); else T_s = +infinity.
+ * *nnz is the number of weights S will hold: those comparing below T_min
+ * or above T_max, and those whose sensitivity is above T_s.  Ranges:
+ * 0 <= tail_ppm < 500000, 0 <= top_ppm < 1000000.  t_min, t_max (fp16
+ * bits), t_s (may be NULL when sens is) and nnz are HOST outputs; the call
+ * synchronises `stream`.
  */
-sqllm_status sqllm_outlier_thresholds(const uint16_t *w, int64_t rows, int64_t cols, int tail_ppm, void *workspace,
-                                      size_t workspace_bytes, uint16_t *t_min, uint16_t *t_max, int64_t *nnz,
-                                      hipStream_t stream);
+sqllm_status sqllm_outlier_thresholds(const uint16_t *w, const float *sens, int64_t rows, int64_t cols, int tail_ppm,
+                                      int top_ppm, void *workspace, size_t workspace_bytes, uint16_t *t_min,
+                                      uint16_t *t_max, float *t_s, int64_t *nnz, hipStream_t stream);
 
 /*
- * sqllm_outlier_extract: S = the weights below t_min or above t_max as CSR
- * (row_ptr int32 [rows + 1]; col_idx uint16 and val fp16 [nnz], columns
- * ascending within a row) and D = W with zeros at S's entries (fp16
- * [rows][cols], must not overlap W).  Writes past nnz_capacity are dropped
- * and reported as SQLLM_ERR_CAPACITY; the call synchronises `stream`.
+ * sqllm_outlier_extract: S = the weights below t_min or above t_max, or
+ * (sens given) with sensitivity above t_s, as CSR (row_ptr int32
+ * [rows + 1]; col_idx uint16 and val fp16 [nnz], columns ascending within a
+ * row) and D = W with zeros at S's entries (fp16 [rows][cols], must not
+ * overlap W).  sens_dense (optional, needs sens): the sensitivities with
+ * zeros at S's entries, the weights to give sqllm_kmeans_lut so that S's
+ * positions take no part in D's clustering.  Writes past nnz_capacity are
+ * dropped and reported as SQLLM_ERR_CAPACITY; the call synchronises
+ * `stream`.
  */
-sqllm_status sqllm_outlier_extract(const uint16_t *w, int64_t rows, int64_t cols, uint16_t t_min, uint16_t t_max,
-                                   int32_t *row_ptr, uint16_t *col_idx, uint16_t *val, int64_t nnz_capacity,
-                                   uint16_t *dense, void *workspace, size_t workspace_bytes, hipStream_t stream);
+sqllm_status sqllm_outlier_extract(const uint16_t *w, const float *sens, int64_t rows, int64_t cols, uint16_t t_min,
+                                   uint16_t t_max, float t_s, int32_t *row_ptr, uint16_t *col_idx, uint16_t *val,
+                                   int64_t nnz_capacity, uint16_t *dense, float *sens_dense, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * sqllm_kmeans_lut: per row of D, 2^bits centroids by `iters` k-means steps

@@ -58,11 +58,12 @@ _lib.sqllm_dense_sparse_gemv_group.argtypes = [ctypes.POINTER(Product), _i32, _i
 _lib.sqllm_quantize_workspace_bytes.restype = _sz
 _lib.sqllm_quantize_workspace_bytes.argtypes = [_i64, _i64]
 _lib.sqllm_outlier_thresholds.restype = _i32
-_lib.sqllm_outlier_thresholds.argtypes = [_vp, _i64, _i64, _i32, _vp, _sz, ctypes.POINTER(ctypes.c_uint16),
-                                          ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(_i64), _vp]
+_lib.sqllm_outlier_thresholds.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _sz, ctypes.POINTER(ctypes.c_uint16),
+                                          ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(_i64), _vp]
 _lib.sqllm_outlier_extract.restype = _i32
-_lib.sqllm_outlier_extract.argtypes = [_vp, _i64, _i64, ctypes.c_uint16, ctypes.c_uint16, _vp, _vp, _vp, _i64, _vp,
-                                       _vp, _sz, _vp]
+_lib.sqllm_outlier_extract.argtypes = [_vp, _vp, _i64, _i64, ctypes.c_uint16, ctypes.c_uint16, ctypes.c_float, _vp,
+                                       _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.sqllm_kmeans_lut.restype = _i32
 _lib.sqllm_kmeans_lut.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp]
 _lib.sqllm_test_unpack.restype = _i32
@@ -254,29 +255,44 @@ def _quantize_ws(rows: int, cols: int, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def outlier_thresholds(w: torch.Tensor, tail_ppm: int = 2000, stream=None):
-    """(T_min, T_max, nnz) of an fp16 [rows, cols] weight matrix (fp16 bit patterns as ints; synchronises)."""
+def outlier_thresholds(w: torch.Tensor, tail_ppm: int = 2000, sens: torch.Tensor | None = None, top_ppm: int = 0,
+                       stream=None):
+    """(T_min, T_max, T_s, nnz) of an fp16 [rows, cols] weight matrix: fp16
+    bit patterns as ints, T_s a float (+inf without sensitivities); synchronises."""
     rows, cols = w.shape
     ws = _quantize_ws(rows, cols, w.device)
-    lo, hi, nnz = ctypes.c_uint16(), ctypes.c_uint16(), ctypes.c_int64()
-    _check(_lib.sqllm_outlier_thresholds(_dev(w, "w", torch.float16), rows, cols, tail_ppm, ws.data_ptr(), ws.numel(),
-                                         ctypes.byref(lo), ctypes.byref(hi), ctypes.byref(nnz), _stream(stream)),
+    lo, hi, ts, nnz = ctypes.c_uint16(), ctypes.c_uint16(), ctypes.c_float(), ctypes.c_int64()
+    sp = None if sens is None else _dev(sens, "sens", torch.float32)
+    _check(_lib.sqllm_outlier_thresholds(_dev(w, "w", torch.float16), sp, rows, cols, tail_ppm, top_ppm,
+                                         ws.data_ptr(), ws.numel(), ctypes.byref(lo), ctypes.byref(hi),
+                                         ctypes.byref(ts), ctypes.byref(nnz), _stream(stream)),
            "sqllm_outlier_thresholds")
-    return lo.value, hi.value, nnz.value
+    return lo.value, hi.value, ts.value, nnz.value
 
 
-def outlier_extract(w: torch.Tensor, t_min: int, t_max: int, nnz: int, stream=None):
-    """W = D + S: (row_ptr int32, col int16 bits, val fp16, dense fp16) (synchronises)."""
+def outlier_extract(w: torch.Tensor, t_min: int, t_max: int, nnz: int, sens: torch.Tensor | None = None,
+                    t_s: float = float("inf"), stream=None):
+    """W = D + S: (row_ptr int32, col int16 bits, val fp16, dense fp16, and,
+    given sens, the sensitivities with zeros at S's entries); synchronises."""
     rows, cols = w.shape
     ws = _quantize_ws(rows, cols, w.device)
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=w.device)
     col = torch.empty(max(nnz, 1), dtype=torch.int16, device=w.device)
     val = torch.empty(max(nnz, 1), dtype=torch.float16, device=w.device)
     dense = torch.empty_like(w)
-    _check(_lib.sqllm_outlier_extract(_dev(w, "w", torch.float16), rows, cols, t_min, t_max, row_ptr.data_ptr(),
-                                      col.data_ptr(), val.data_ptr(), nnz, _dev(dense, "dense", torch.float16),
-                                      ws.data_ptr(), ws.numel(), _stream(stream)), "sqllm_outlier_extract")
-    return row_ptr, col[:nnz], val[:nnz], dense
+    sp = sd = None
+    sens_dense = None
+    if sens is not None:
+        sp = _dev(sens, "sens", torch.float32)
+        sens_dense = torch.empty_like(sens)
+        sd = sens_dense.data_ptr()
+    _check(_lib.sqllm_outlier_extract(_dev(w, "w", torch.float16), sp, rows, cols, t_min, t_max, t_s,
+                                      row_ptr.data_ptr(), col.data_ptr(), val.data_ptr(), nnz,
+                                      _dev(dense, "dense", torch.float16), sd, ws.data_ptr(), ws.numel(),
+                                      _stream(stream)), "sqllm_outlier_extract")
+    if sens is None:
+        return row_ptr, col[:nnz], val[:nnz], dense
+    return row_ptr, col[:nnz], val[:nnz], dense, sens_dense
 
 
 def kmeans_lut(dense: torch.Tensor, bits: int, iters: int = 20, sens: torch.Tensor | None = None, stream=None):

@@ -366,7 +366,7 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
 
 namespace {
 constexpr size_t kBinsBytes = 65536 * 4;
-constexpr size_t kMiscBytes = 256; // keys, total, overflow flag
+constexpr size_t kMiscBytes = 256; // rank selection (64 B), total, overflow flag
 
 sqllm_status quantize_shape(const void *w, int64_t rows, int64_t cols)
 {
@@ -383,57 +383,86 @@ size_t sqllm_quantize_workspace_bytes(int64_t rows, int64_t cols)
     return kBinsBytes + kMiscBytes + (size_t)rows * 4;
 }
 
-sqllm_status sqllm_outlier_thresholds(const uint16_t *w, int64_t rows, int64_t cols, int tail_ppm, void *workspace,
-                                      size_t workspace_bytes, uint16_t *t_min, uint16_t *t_max, int64_t *nnz,
-                                      hipStream_t stream)
+namespace {
+// IEEE total order key back to the bit pattern (binary16 / binary32).
+uint16_t f16_from_key(uint32_t k) { return (uint16_t)((k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu)); }
+uint32_t f32_from_key(uint32_t k) { return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k; }
+
+int64_t rank_of(int64_t n, int ppm) // floor(n * ppm / 1e6) without overflow
+{
+    return (n / 1000000) * ppm + ((n % 1000000) * ppm) / 1000000;
+}
+} // namespace
+
+sqllm_status sqllm_outlier_thresholds(const uint16_t *w, const float *sens, int64_t rows, int64_t cols, int tail_ppm,
+                                      int top_ppm, void *workspace, size_t workspace_bytes, uint16_t *t_min,
+                                      uint16_t *t_max, float *t_s, int64_t *nnz, hipStream_t stream)
 {
     sqllm_status st = quantize_shape(w, rows, cols);
     if (st != SQLLM_OK) return st;
-    if (!t_min || !t_max || !nnz) return SQLLM_ERR_NULL;
+    if (!t_min || !t_max || !nnz || (sens && !t_s)) return SQLLM_ERR_NULL;
     if (tail_ppm < 0 || tail_ppm >= 500000) return SQLLM_ERR_SHAPE;
+    if (sens && (top_ppm < 0 || top_ppm >= 1000000)) return SQLLM_ERR_SHAPE;
+    if (sens && !aligned(sens, 4)) return SQLLM_ERR_ALIGN;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < sqllm_quantize_workspace_bytes(rows, cols))
         return SQLLM_ERR_WORKSPACE;
     const int64_t n = rows * cols;
-    const int64_t tail = (n / 1000000) * tail_ppm + ((n % 1000000) * tail_ppm) / 1000000;
+    const int64_t tail = rank_of(n, tail_ppm);
     uint32_t *bins = (uint32_t *)workspace;
-    uint32_t *keys = (uint32_t *)((char *)workspace + kBinsBytes);
+    SelectOut *sel = (SelectOut *)((char *)workspace + kBinsBytes);
     unsigned long long *total = (unsigned long long *)((char *)workspace + kBinsBytes + 64);
     int32_t *counts = (int32_t *)((char *)workspace + kBinsBytes + kMiscBytes);
-    uint32_t hk[2] = {0, 0};
-    unsigned long long ht = 0;
-    if (launch_thresholds(w, n, tail, bins, keys, stream) != hipSuccess ||
-        hipMemcpyAsync(hk, keys, sizeof(hk), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
+    SelectOut hw{}, hs{};
+    if (launch_rank_select(w, false, n, tail, n - 1 - tail, bins, sel, stream) != hipSuccess ||
+        hipMemcpyAsync(&hw, sel, sizeof(hw), hipMemcpyDeviceToHost, stream) != hipSuccess)
         return SQLLM_ERR_HIP;
+    if (sens) {
+        const int64_t r = n - 1 - rank_of(n, top_ppm); // one rank: the fp32 passes select a single value
+        if (launch_rank_select(sens, true, n, r, r, bins, sel, stream) != hipSuccess ||
+            hipMemcpyAsync(&hs, sel, sizeof(hs), hipMemcpyDeviceToHost, stream) != hipSuccess)
+            return SQLLM_ERR_HIP;
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess) return SQLLM_ERR_HIP;
+    const uint16_t lo = f16_from_key(hw.bin[0]), hi = f16_from_key(hw.bin[1]);
+    float ts = __builtin_inff();
+    if (sens) {
+        const uint32_t bits = f32_from_key((hs.bin[0] << 16) | hs.bin2[0]);
+        __builtin_memcpy(&ts, &bits, 4);
+    }
+    unsigned long long ht = 0;
     if (hipMemsetAsync(total, 0, sizeof(*total), stream) != hipSuccess ||
-        launch_outlier_count(w, (int)rows, (int)cols, (uint16_t)hk[0], (uint16_t)hk[1], counts, total, stream) !=
-            hipSuccess ||
+        launch_outlier_count(w, sens, (int)rows, (int)cols, lo, hi, ts, counts, total, stream) != hipSuccess ||
         hipMemcpyAsync(&ht, total, sizeof(ht), hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return SQLLM_ERR_HIP;
-    *t_min = (uint16_t)hk[0];
-    *t_max = (uint16_t)hk[1];
+    *t_min = lo;
+    *t_max = hi;
+    if (t_s) *t_s = ts;
     *nnz = (int64_t)ht;
     return SQLLM_OK;
 }
 
-sqllm_status sqllm_outlier_extract(const uint16_t *w, int64_t rows, int64_t cols, uint16_t t_min, uint16_t t_max,
-                                   int32_t *row_ptr, uint16_t *col_idx, uint16_t *val, int64_t nnz_capacity,
-                                   uint16_t *dense, void *workspace, size_t workspace_bytes, hipStream_t stream)
+sqllm_status sqllm_outlier_extract(const uint16_t *w, const float *sens, int64_t rows, int64_t cols, uint16_t t_min,
+                                   uint16_t t_max, float t_s, int32_t *row_ptr, uint16_t *col_idx, uint16_t *val,
+                                   int64_t nnz_capacity, uint16_t *dense, float *sens_dense, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
 {
     sqllm_status st = quantize_shape(w, rows, cols);
     if (st != SQLLM_OK) return st;
-    if (!row_ptr || !dense || (nnz_capacity > 0 && (!col_idx || !val))) return SQLLM_ERR_NULL;
+    if (!row_ptr || !dense || (nnz_capacity > 0 && (!col_idx || !val)) || (sens_dense && !sens))
+        return SQLLM_ERR_NULL;
     if (nnz_capacity < 0) return SQLLM_ERR_SHAPE;
-    if (!aligned(row_ptr, 4) || !aligned(dense, 2)) return SQLLM_ERR_ALIGN;
+    if (!aligned(row_ptr, 4) || !aligned(dense, 2) || (sens && !aligned(sens, 4)) ||
+        (sens_dense && !aligned(sens_dense, 4)))
+        return SQLLM_ERR_ALIGN;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < sqllm_quantize_workspace_bytes(rows, cols))
         return SQLLM_ERR_WORKSPACE;
     int *overflow = (int *)((char *)workspace + kBinsBytes + 128);
     int32_t *counts = (int32_t *)((char *)workspace + kBinsBytes + kMiscBytes);
     int hov = 0;
     if (hipMemsetAsync(overflow, 0, sizeof(int), stream) != hipSuccess ||
-        launch_outlier_extract(w, (int)rows, (int)cols, t_min, t_max, counts, row_ptr, col_idx, val, nnz_capacity,
-                               dense, overflow, stream) != hipSuccess ||
+        launch_outlier_extract(w, sens, (int)rows, (int)cols, t_min, t_max, t_s, counts, row_ptr, col_idx, val,
+                               nnz_capacity, dense, sens_dense, overflow, stream) != hipSuccess ||
         hipMemcpyAsync(&hov, overflow, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return SQLLM_ERR_HIP;

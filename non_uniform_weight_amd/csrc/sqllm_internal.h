@@ -55,13 +55,25 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
                                hipStream_t stream);
 hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mode mode, const LaunchShape &ls,
                                      hipStream_t stream);
-hipError_t launch_thresholds(const uint16_t *w, int64_t n, int64_t tail, uint32_t *bins, uint32_t *keys,
-                             hipStream_t stream);
-hipError_t launch_outlier_count(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
-                                int32_t *counts, unsigned long long *total, hipStream_t stream);
-hipError_t launch_outlier_extract(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
-                                  int32_t *counts, int32_t *row_ptr, uint16_t *col_idx, uint16_t *val,
-                                  int64_t capacity, uint16_t *dense, int *overflow, hipStream_t stream);
+// Rank selection over 16-bit keys: bin and rank within the bin of ranks r0,
+// r1 (fp16 order keys), or of the high then low key halves (fp32).
+struct SelectOut {
+    uint32_t bin[2];
+    uint32_t pad0[2];
+    int64_t rest[2];
+    uint32_t bin2[2];
+    uint32_t pad1[2];
+    int64_t rest2[2];
+};
+hipError_t launch_rank_select(const void *src, bool fp32, int64_t n, int64_t r0, int64_t r1, uint32_t *bins,
+                              SelectOut *out, hipStream_t stream);
+hipError_t launch_outlier_count(const uint16_t *w, const float *sens, int rows, int cols, uint16_t t_min,
+                                uint16_t t_max, float t_s, int32_t *counts, unsigned long long *total,
+                                hipStream_t stream);
+hipError_t launch_outlier_extract(const uint16_t *w, const float *sens, int rows, int cols, uint16_t t_min,
+                                  uint16_t t_max, float t_s, int32_t *counts, int32_t *row_ptr, uint16_t *col_idx,
+                                  uint16_t *val, int64_t capacity, uint16_t *dense, float *sens_dense, int *overflow,
+                                  hipStream_t stream);
 hipError_t launch_kmeans(const uint16_t *dense, const float *sens, int rows, int cols, int bits, int iters,
                          uint8_t *codes, uint16_t *lut, hipStream_t stream);
 hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void *packed, int *bad, hipStream_t stream);

@@ -8,8 +8,12 @@
 // Split: T_min / T_max are the values of rank floor(n p) from either end of
 // the matrix's fp16 values in IEEE total order (-0 before +0), found exactly
 // from a 65536-bin histogram of the bit patterns (one bin per fp16 value);
-// a weight is an outlier when it compares below T_min or above T_max.
-// Outliers go to CSR (columns ascending), D keeps the rest with zeros there.
+// a weight is an outlier when it compares below T_min or above T_max.  With
+// sensitivities, T_s is the fp32 sensitivity of rank n - 1 - n_top, found
+// exactly from two 16-bit histogram passes (high key halves, then low halves
+// within the chosen high half), and a weight whose sensitivity is above T_s
+// goes to S as well.  S goes to CSR (columns ascending), D keeps the rest
+// with zeros there.
 //
 // k-means: one workgroup per row.  Centroids start uniformly spaced over the
 // row's range; each step assigns every weight to the nearest centroid (the
@@ -29,24 +33,38 @@ namespace {
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-// IEEE total order of binary16 bit patterns as an unsigned key.
+// IEEE total order of binary16 / binary32 bit patterns as unsigned keys.
 __device__ __forceinline__ uint32_t order_key(uint32_t b) { return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u); }
-__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu); }
+__device__ __forceinline__ uint32_t order_key32(uint32_t b) { return (b & 0x80000000u) ? ~b : (b | 0x80000000u); }
 
 constexpr int kHistThreads = 512;
 constexpr int kHistChunk = 65535; // values per workgroup: a 16-bit LDS counter cannot overflow
 
-// Histogram of the fp16 values by order key: per-workgroup LDS counters
-// (two 16-bit counts per word), added into the global 65536 bins.
-__global__ void __launch_bounds__(kHistThreads) hist_kernel(const uint16_t *__restrict__ w, int64_t n,
+enum HistMode { kHistF16 = 0, kHistF32High = 1, kHistF32Low = 2 };
+
+// Histogram of 16-bit keys: the fp16 order key, the high half of the fp32
+// order key, or the low half of the fp32 keys whose high half is *sel.
+// Per-workgroup LDS counters (two 16-bit counts per word) added into the
+// global 65536 bins.
+template <int MODE>
+__global__ void __launch_bounds__(kHistThreads) hist_kernel(const void *__restrict__ src, int64_t n,
+                                                            const uint32_t *__restrict__ sel,
                                                             uint32_t *__restrict__ bins)
 {
     __shared__ uint32_t h[32768];
     for (int i = threadIdx.x; i < 32768; i += kHistThreads) h[i] = 0;
+    const uint32_t want = MODE == kHistF32Low ? *sel : 0u;
     __syncthreads();
     const int64_t beg = (int64_t)blockIdx.x * kHistChunk, end = min(beg + kHistChunk, n);
     for (int64_t i = beg + threadIdx.x; i < end; i += kHistThreads) {
-        const uint32_t k = order_key(w[i]);
+        uint32_t k;
+        if (MODE == kHistF16) {
+            k = order_key(((const uint16_t *)src)[i]);
+        } else {
+            const uint32_t k32 = order_key32(((const uint32_t *)src)[i]);
+            if (MODE == kHistF32Low && (k32 >> 16) != want) continue;
+            k = MODE == kHistF32High ? k32 >> 16 : k32 & 0xFFFFu;
+        }
         atomicAdd(&h[k >> 1], 1u << (16 * (k & 1)));
     }
     __syncthreads();
@@ -57,9 +75,12 @@ __global__ void __launch_bounds__(kHistThreads) hist_kernel(const uint16_t *__re
     }
 }
 
-// Keys of ranks r0 and r1 (ascending) from the histogram; one workgroup.
+// For ranks r[0], r[1] (ascending, from `rank` in device memory when given,
+// else r0 / r1): the bin holding that rank and the rank within the bin.
+// One workgroup.
 __global__ void __launch_bounds__(1024) select_kernel(const uint32_t *__restrict__ bins, int64_t r0, int64_t r1,
-                                                      uint32_t *__restrict__ out)
+                                                      const int64_t *__restrict__ rank,
+                                                      uint32_t *__restrict__ out_bin, int64_t *__restrict__ out_rest)
 {
     __shared__ int64_t part[1024];
     const int t = threadIdx.x;
@@ -76,36 +97,41 @@ __global__ void __launch_bounds__(1024) select_kernel(const uint32_t *__restrict
     }
     const int64_t before = t > 0 ? part[t - 1] : 0;
     for (int q = 0; q < 2; ++q) {
-        const int64_t r = q == 0 ? r0 : r1;
+        const int64_t r = rank ? rank[q] : (q == 0 ? r0 : r1);
         if (before <= r && r < part[t]) {
             int64_t c = before;
             for (int i = 0; i < 64; ++i) {
-                c += bins[t * 64 + i];
-                if (r < c) {
-                    out[q] = key_bits((uint32_t)(t * 64 + i));
+                const int64_t next = c + bins[t * 64 + i];
+                if (r < next) {
+                    out_bin[q] = (uint32_t)(t * 64 + i);
+                    out_rest[q] = r - c;
                     break;
                 }
+                c = next;
             }
         }
     }
 }
 
-__device__ __forceinline__ bool is_outlier(uint16_t b, float lo, float hi)
+// Whether a weight goes to S: outside [lo, hi], or more sensitive than t_s.
+__device__ __forceinline__ bool to_sparse(uint16_t b, float lo, float hi, const float *srow, int c, float t_s)
 {
     const float v = h2f(b);
-    return v < lo || v > hi;
+    return v < lo || v > hi || (srow && srow[c] > t_s);
 }
 
-// Outliers per row (one workgroup per row) and their total.
-__global__ void __launch_bounds__(256) count_kernel(const uint16_t *__restrict__ w, int cols, uint16_t t_min,
-                                                    uint16_t t_max, int32_t *__restrict__ counts,
+// Entries of S per row (one workgroup per row) and their total.
+__global__ void __launch_bounds__(256) count_kernel(const uint16_t *__restrict__ w, const float *__restrict__ sens,
+                                                    int cols, uint16_t t_min, uint16_t t_max, float t_s,
+                                                    int32_t *__restrict__ counts,
                                                     unsigned long long *__restrict__ total)
 {
     __shared__ int part[4];
     const float lo = h2f(t_min), hi = h2f(t_max);
     const uint16_t *row = w + (int64_t)blockIdx.x * cols;
+    const float *srow = sens ? sens + (int64_t)blockIdx.x * cols : nullptr;
     int c = 0;
-    for (int i = threadIdx.x; i < cols; i += 256) c += is_outlier(row[i], lo, hi);
+    for (int i = threadIdx.x; i < cols; i += 256) c += to_sparse(row[i], lo, hi, srow, i, t_s);
     for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
     __syncthreads();
@@ -142,26 +168,30 @@ __global__ void __launch_bounds__(1024) scan_kernel(const int32_t *__restrict__ 
     if (t == 1023) row_ptr[rows] = (int32_t)part[1023];
 }
 
-// CSR entries of each row in column order and D (one workgroup of four
-// waves per row, 256 columns per step).  Entries past the capacity are
-// dropped and flagged.
-__global__ void __launch_bounds__(256) fill_kernel(const uint16_t *__restrict__ w, int cols, uint16_t t_min,
-                                                   uint16_t t_max, const int32_t *__restrict__ row_ptr,
+// CSR entries of each row in column order, D, and (when asked) the
+// sensitivities with zeros at S's entries; one workgroup of four waves per
+// row, 256 columns per step.  Entries past the capacity are dropped and
+// flagged.
+__global__ void __launch_bounds__(256) fill_kernel(const uint16_t *__restrict__ w, const float *__restrict__ sens,
+                                                   int cols, uint16_t t_min, uint16_t t_max, float t_s,
+                                                   const int32_t *__restrict__ row_ptr,
                                                    uint16_t *__restrict__ col_idx, uint16_t *__restrict__ val,
                                                    int64_t capacity, uint16_t *__restrict__ dense,
-                                                   int *__restrict__ overflow)
+                                                   float *__restrict__ sens_dense, int *__restrict__ overflow)
 {
     __shared__ int wave_n[4];
     const float lo = h2f(t_min), hi = h2f(t_max);
     const int64_t r = blockIdx.x;
     const uint16_t *row = w + r * cols;
+    const float *srow = sens ? sens + r * cols : nullptr;
     uint16_t *drow = dense + r * cols;
+    float *sdrow = sens_dense ? sens_dense + r * cols : nullptr;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int64_t base = row_ptr[r];
     for (int c0 = 0; c0 < cols; c0 += 256) {
         const int c = c0 + threadIdx.x;
         const uint16_t b = c < cols ? row[c] : 0;
-        const bool out = c < cols && is_outlier(b, lo, hi);
+        const bool out = c < cols && to_sparse(b, lo, hi, srow, c, t_s);
         const uint64_t m = __ballot(out);
         const int before_lane = __popcll(m & ((1ull << lane) - 1));
         if (lane == 0) wave_n[wv] = __popcll(m);
@@ -169,7 +199,10 @@ __global__ void __launch_bounds__(256) fill_kernel(const uint16_t *__restrict__ 
         int before_wave = 0;
         for (int k = 0; k < wv; ++k) before_wave += wave_n[k];
         const int step_n = wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
-        if (c < cols) drow[c] = out ? (uint16_t)0 : b;
+        if (c < cols) {
+            drow[c] = out ? (uint16_t)0 : b;
+            if (sdrow) sdrow[c] = out ? 0.f : srow[c];
+        }
         if (out) {
             const int64_t at = base + before_wave + before_lane;
             if (at < capacity) {
@@ -289,33 +322,50 @@ __global__ void __launch_bounds__(kKmThreads) kmeans_kernel(const uint16_t *__re
 
 } // namespace
 
-hipError_t launch_thresholds(const uint16_t *w, int64_t n, int64_t tail, uint32_t *bins, uint32_t *keys,
-                             hipStream_t stream)
+hipError_t launch_rank_select(const void *src, bool fp32, int64_t n, int64_t r0, int64_t r1, uint32_t *bins,
+                              SelectOut *out, hipStream_t stream)
 {
+    const unsigned blocks = (unsigned)((n + kHistChunk - 1) / kHistChunk);
     if (hipMemsetAsync(bins, 0, 65536 * sizeof(uint32_t), stream) != hipSuccess) return hipGetLastError();
-    const int64_t blocks = (n + kHistChunk - 1) / kHistChunk;
-    hipLaunchKernelGGL(hist_kernel, dim3((unsigned)blocks), dim3(kHistThreads), 0, stream, w, n, bins);
-    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(1024), 0, stream, bins, tail, n - 1 - tail, keys);
+    if (!fp32) {
+        hipLaunchKernelGGL(hist_kernel<kHistF16>, dim3(blocks), dim3(kHistThreads), 0, stream, src, n,
+                           (const uint32_t *)nullptr, bins);
+        hipLaunchKernelGGL(select_kernel, dim3(1), dim3(1024), 0, stream, bins, r0, r1, (const int64_t *)nullptr,
+                           out->bin, out->rest);
+        return hipGetLastError();
+    }
+    // high halves of the keys, then the low halves within the selected high half
+    hipLaunchKernelGGL(hist_kernel<kHistF32High>, dim3(blocks), dim3(kHistThreads), 0, stream, src, n,
+                       (const uint32_t *)nullptr, bins);
+    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(1024), 0, stream, bins, r0, r1, (const int64_t *)nullptr,
+                       out->bin, out->rest);
+    if (hipMemsetAsync(bins, 0, 65536 * sizeof(uint32_t), stream) != hipSuccess) return hipGetLastError();
+    hipLaunchKernelGGL(hist_kernel<kHistF32Low>, dim3(blocks), dim3(kHistThreads), 0, stream, src, n,
+                       (const uint32_t *)out->bin, bins);
+    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(1024), 0, stream, bins, (int64_t)0, (int64_t)0,
+                       (const int64_t *)out->rest, out->bin2, out->rest2);
     return hipGetLastError();
 }
 
-hipError_t launch_outlier_count(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
-                                int32_t *counts, unsigned long long *total, hipStream_t stream)
+hipError_t launch_outlier_count(const uint16_t *w, const float *sens, int rows, int cols, uint16_t t_min,
+                                uint16_t t_max, float t_s, int32_t *counts, unsigned long long *total,
+                                hipStream_t stream)
 {
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, cols, t_min, t_max, counts,
-                       total);
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, sens, cols, t_min, t_max, t_s,
+                       counts, total);
     return hipGetLastError();
 }
 
-hipError_t launch_outlier_extract(const uint16_t *w, int rows, int cols, uint16_t t_min, uint16_t t_max,
-                                  int32_t *counts, int32_t *row_ptr, uint16_t *col_idx, uint16_t *val,
-                                  int64_t capacity, uint16_t *dense, int *overflow, hipStream_t stream)
+hipError_t launch_outlier_extract(const uint16_t *w, const float *sens, int rows, int cols, uint16_t t_min,
+                                  uint16_t t_max, float t_s, int32_t *counts, int32_t *row_ptr, uint16_t *col_idx,
+                                  uint16_t *val, int64_t capacity, uint16_t *dense, float *sens_dense, int *overflow,
+                                  hipStream_t stream)
 {
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, cols, t_min, t_max, counts,
-                       (unsigned long long *)nullptr);
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, sens, cols, t_min, t_max, t_s,
+                       counts, (unsigned long long *)nullptr);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, counts, rows, row_ptr);
-    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, cols, t_min, t_max, row_ptr,
-                       col_idx, val, capacity, dense, overflow);
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)rows), dim3(256), 0, stream, w, sens, cols, t_min, t_max, t_s,
+                       row_ptr, col_idx, val, capacity, dense, sens_dense, overflow);
     return hipGetLastError();
 }
 

@@ -171,7 +171,7 @@ def test_tuning_hook_bounds(lib):
 
 def test_quantize_argument_errors(lib):
     u16 = ctypes.c_uint16
-    lo, hi, nnz = u16(), u16(), ctypes.c_int64()
+    lo, hi, ts, nnz = u16(), u16(), ctypes.c_float(), ctypes.c_int64()
     ws = P(0x200000)
     wsb = lib.sqllm_quantize_workspace_bytes(64, 256)
     assert wsb == 65536 * 4 + 256 + 64 * 4
@@ -179,26 +179,34 @@ def test_quantize_argument_errors(lib):
     assert lib.sqllm_quantize_workspace_bytes(1 << 20, 4096) == 0       # more than 2^31 - 1 weights
     assert lib.sqllm_quantize_workspace_bytes(0, 256) == 0
 
-    def thr(w=A16, rows=64, cols=256, ppm=2000, ws=ws, wsb=wsb, out=True):
-        refs = (ctypes.byref(lo), ctypes.byref(hi), ctypes.byref(nnz)) if out else (None, None, None)
-        return lib.sqllm_outlier_thresholds(w, rows, cols, ppm, ws, wsb, *refs, None)
+    def thr(w=A16, sens=None, rows=64, cols=256, ppm=2000, top=500, ws=ws, wsb=wsb, out=True, t_s=True):
+        refs = (ctypes.byref(lo), ctypes.byref(hi)) if out else (None, None)
+        return lib.sqllm_outlier_thresholds(w, sens, rows, cols, ppm, top, ws, wsb, *refs,
+                                            ctypes.byref(ts) if t_s else None, ctypes.byref(nnz), None)
     assert thr(w=None) == 1
     assert thr(out=False) == 1
+    assert thr(sens=B16, t_s=False) == 1                                  # T_s needs somewhere to go
     assert thr(cols=65537) == 3
     assert thr(ppm=500000) == 3
     assert thr(ppm=-1) == 3
+    assert thr(sens=B16, top=1000000) == 3
+    assert thr(sens=B16, top=-1) == 3
     assert thr(w=P(0x100001)) == 5
+    assert thr(sens=P(0x200002)) == 5
     assert thr(ws=None) == 8
     assert thr(ws=P(0x200080)) == 8                                      # not 256-byte aligned
     assert thr(wsb=wsb - 1) == 8
 
-    def ext(w=A16, rp=A16, cap=10, col=B16, dense=B16, ws=ws, wsb=wsb):
-        return lib.sqllm_outlier_extract(w, 64, 256, 0x8000, 0, rp, col, B16, cap, dense, ws, wsb, None)
+    def ext(w=A16, sens=None, rp=A16, cap=10, col=B16, dense=B16, sd=None, ws=ws, wsb=wsb):
+        return lib.sqllm_outlier_extract(w, sens, 64, 256, 0x8000, 0, 1.0, rp, col, B16, cap, dense, sd, ws, wsb,
+                                         None)
     assert ext(rp=None) == 1
     assert ext(dense=None) == 1
     assert ext(col=None) == 1
+    assert ext(sd=B16) == 1                                               # zeroed sensitivities need sens
     assert ext(cap=-1) == 3
     assert ext(rp=P(0x100002)) == 5
+    assert ext(sens=B16, sd=P(0x200002)) == 5
     assert ext(wsb=0) == 8
 
     def km(d=A16, bits=3, iters=10, codes=B16, lut=B16, sens=None):

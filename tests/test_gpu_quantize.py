@@ -29,11 +29,43 @@ def heavy(tag, rows, cols, df=4, scale=0.02):
 
 def split_on_gpu(w, ppm):
     wd = u16_to_dev(w)
-    t_min, t_max, nnz = nw().outlier_thresholds(wd, ppm)
+    t_min, t_max, t_s, nnz = nw().outlier_thresholds(wd, ppm)
+    assert t_s == float("inf")
     rp, col, val, dense = nw().outlier_extract(wd, t_min, t_max, nnz)
     torch.cuda.synchronize()
     return (t_min, t_max, nnz, rp.cpu().numpy(), dev_to_u16(col) if nnz else np.zeros(0, np.uint16),
             dev_to_u16(val) if nnz else np.zeros(0, np.uint16), dev_to_u16(dense))
+
+
+def split_sens_on_gpu(w, sens, ppm, top_ppm):
+    """(t_min, t_max, t_s, nnz), (row_ptr, col, val, dense, sens_dense) as numpy."""
+    wd, sd = u16_to_dev(w), torch.from_numpy(sens).cuda()
+    t_min, t_max, t_s, nnz = nw().outlier_thresholds(wd, ppm, sd, top_ppm)
+    rp, col, val, dense, sdense = nw().outlier_extract(wd, t_min, t_max, nnz, sd, t_s)
+    torch.cuda.synchronize()
+    arrays = (rp.cpu().numpy(), dev_to_u16(col) if nnz else np.zeros(0, np.uint16),
+              dev_to_u16(val) if nnz else np.zeros(0, np.uint16), dev_to_u16(dense), sdense.cpu().numpy())
+    return (t_min, t_max, np.float32(t_s), nnz), arrays
+
+
+def fisher_like(tag, rows, cols):
+    """Non-negative, heavy-tailed sensitivities (squared normal times a
+    log-normal per row), fp32."""
+    rng = np.random.default_rng(stable_seed(tag))
+    g = rng.normal(0, 1, (rows, cols)) * np.exp(rng.normal(0, 1, (rows, 1)))
+    return (g * g).astype(np.float32)
+
+
+def check_split_sens(w, sens, ppm, top_ppm):
+    got, arrays = split_sens_on_gpu(w, sens, ppm, top_ppm)
+    t_min, t_max, t_s, nnz = q.split_thresholds(w, ppm, sens, top_ppm)
+    assert got[0] == t_min and got[1] == t_max and got[3] == nnz
+    assert got[2].view(np.uint32) == np.float32(t_s).view(np.uint32)
+    want = q.extract(w, t_min, t_max, sens, t_s)
+    for g, e in zip(arrays[:4], want):
+        assert np.array_equal(g, e)
+    assert np.array_equal(arrays[4].view(np.uint32), q.dense_sensitivity(sens, want[0], want[1]).view(np.uint32))
+    return nnz
 
 
 SPLIT_CASES = [(1, 1, 0), (1, 7, 250000), (37, 300, 2250), (130, 1000, 250), (130, 1000, 20000), (257, 4096, 2250),
@@ -106,6 +138,55 @@ def test_split_full_layer_rank_property():
     assert nnz == want[1].size
     assert 0.004 < nnz / n < 0.005
     for g, e in zip((rp, col, val, dense), want):
+        assert np.array_equal(g, e)
+
+
+@pytest.mark.parametrize("rows,cols,ppm,top_ppm", [(1, 9, 100000, 200000), (37, 300, 2000, 500),
+                                                    (130, 1000, 2000, 5000), (257, 4096, 2000, 500),
+                                                    (64, 65536, 2000, 500), (20, 512, 0, 0)])
+def test_split_with_sensitivities_bit_exact(rows, cols, ppm, top_ppm):
+    step(f"split+sens rows={rows} cols={cols} ppm={ppm} top={top_ppm}")
+    w = heavy(f"splits{rows}x{cols}", rows, cols)
+    sens = fisher_like(f"fisher{rows}x{cols}", rows, cols)
+    check_split_sens(w, sens, ppm, top_ppm)
+
+
+def test_split_sensitivity_order_and_ties():
+    """Repeated sensitivities (ties at T_s stay dense), zeros, negative
+    values and -0 (total order), and values that share their high 16 bits."""
+    step("split+sens ties")
+    rows, cols = 16, 640
+    w = heavy("ties", rows, cols)
+    rng = np.random.default_rng(stable_seed("ties-sens"))
+    sens = rng.choice(np.array([0.0, 1.0, 2.0, 3.0], np.float32), (rows, cols))
+    sens[3] = -rng.exponential(1.0, cols).astype(np.float32)
+    sens[4, :10] = -0.0
+    base = np.float32(5.0).view(np.uint32)
+    sens[5] = (base + rng.integers(0, 4096, cols).astype(np.uint32)).view(np.float32)  # one high half
+    for top in (0, 500, 20000, 300000):
+        check_split_sens(w, sens, 2000, top)
+
+
+def test_split_sensitivity_full_layer_rank_property():
+    """LLaMA-65B down projection (8192 x 22016): 0.4% outliers (0.2 / 99.8
+    percentiles) plus the 0.05% most sensitive weights, as on the pages;
+    T_s holds its rank, S is the oracle's given the thresholds."""
+    rows, cols, ppm, top = 8192, 22016, 2000, 500
+    w = heavy("full-split", rows, cols)
+    sens = fisher_like("full-fisher", rows, cols)
+    step(f"split+sens full rows={rows} cols={cols}")
+    got, arrays = split_sens_on_gpu(w, sens, ppm, top)
+    t_min, t_max, t_s, nnz = got
+    n = rows * cols
+    n_top = n * top // 1_000_000
+    keys = q.total_order_key32(sens.ravel().view(np.uint32))
+    k_s = q.total_order_key32(np.array([t_s]).view(np.uint32))[0]
+    assert np.count_nonzero(keys > k_s) <= n_top < np.count_nonzero(keys >= k_s)
+    del keys
+    want = q.extract(w, t_min, t_max, sens, t_s)
+    assert nnz == want[1].size
+    assert 0.0040 < nnz / n < 0.0046          # 0.4% + 0.05%, less the overlap
+    for g, e in zip(arrays[:4], want):
         assert np.array_equal(g, e)
 
 
@@ -194,7 +275,7 @@ def test_split_kmeans_pack_product_pipeline():
     x = np.random.default_rng(stable_seed("pipeline-x")).normal(0, 1, (2, cols)).astype(np.float16).view(np.uint16)
     step("pipeline split/kmeans/pack/product")
     wd = u16_to_dev(w)
-    t_min, t_max, nnz = nw().outlier_thresholds(wd, 2250)
+    t_min, t_max, _, nnz = nw().outlier_thresholds(wd, 2250)
     rp, col, val, dense = nw().outlier_extract(wd, t_min, t_max, nnz)
     codes, lut = nw().kmeans_lut(dense, bits, 20)
     packed = nw().pack(codes, bits)
@@ -206,3 +287,28 @@ def test_split_kmeans_pack_product_pipeline():
     assert np.array_equal(codes.cpu().numpy(), o_codes)
     y_ref, scale = oracle.dense_sparse_gemv(o_codes, o_lut, bits, o_rp, o_col, o_val, x)
     assert_close(y, y_ref, scale, what="pipeline")
+
+
+def test_weighted_pipeline_with_sensitive_values():
+    """The pages' full recipe on one layer: 0.4% outliers + 0.05% sensitive
+    values to S, D clustered with its sensitivities (zero at S), 4-bit,
+    packed and multiplied, against the oracle's own pipeline."""
+    rows, cols, bits = 260, 2048, 4
+    w = heavy("wpipe", rows, cols)
+    sens = fisher_like("wpipe-fisher", rows, cols)
+    x = np.random.default_rng(stable_seed("wpipe-x")).normal(0, 1, (3, cols)).astype(np.float16).view(np.uint16)
+    step("weighted pipeline")
+    wd, sd = u16_to_dev(w), torch.from_numpy(sens).cuda()
+    t_min, t_max, t_s, nnz = nw().outlier_thresholds(wd, 2000, sd, 500)
+    rp, col, val, dense, sdense = nw().outlier_extract(wd, t_min, t_max, nnz, sd, t_s)
+    codes, lut = nw().kmeans_lut(dense, bits, 25, sdense)
+    packed = nw().pack(codes, bits)
+    y = nw().dense_sparse_gemv(packed, lut, bits, rp, col, val, u16_to_dev(x))
+    torch.cuda.synchronize()
+    o_min, o_max, o_s, _ = q.split_thresholds(w, 2000, sens, 500)
+    o_rp, o_col, o_val, o_dense = q.extract(w, o_min, o_max, sens, o_s)
+    o_codes, o_lut = q.kmeans_lut(o_dense, q.dense_sensitivity(sens, o_rp, o_col), bits, 25)
+    assert np.array_equal(dev_to_u16(lut), o_lut)
+    assert np.array_equal(codes.cpu().numpy(), o_codes)
+    y_ref, scale = oracle.dense_sparse_gemv(o_codes, o_lut, bits, o_rp, o_col, o_val, x)
+    assert_close(y, y_ref, scale, what="weighted pipeline")
