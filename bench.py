@@ -55,10 +55,11 @@ def parse():
                    help="level: one group launch per (q,k,v), (o), (gate,up), (down); single: one call per product")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
-    p.add_argument("--ablation", choices=("outliers", "batch"), default=None,
+    p.add_argument("--ablation", choices=("outliers", "batch", "offline"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
-                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8")
+                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8; offline: the "
+                        "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
     return p.parse_args()
@@ -361,6 +362,81 @@ def batch_ablation(args) -> None:
           flush=True)
 
 
+def offline_ablation(args) -> None:
+    """The offline steps on the three LLaMA-65B shapes: thresholds (0.2 / 99.8
+    percentiles and the 0.05% most sensitive), CSR + D extraction, and 3-bit
+    weighted k-means (20 steps) of D.  Inputs: Student-t (4 degrees of
+    freedom) weights x 0.02 and squared-normal sensitivities, drawn on the
+    GPU from a seeded generator.  The split calls synchronise, so they are
+    timed by the host clock around the call; the k-means by HIP events.  The
+    oracle runs the same steps on a slice (split: 512 rows; k-means: 8 rows)
+    of the 8192 x 8192 shape, scaled to the whole matrix by rows."""
+    import numpy as np
+    import torch
+
+    import non_uniform_weight_amd as nw
+
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed + 1234)
+    shapes = [(8192, 8192, 4), (22016, 8192, 2), (8192, 22016, 1)]
+    res, layer_ms = [], 0.0
+    for rows, cols, count in shapes:
+        z = torch.randn((rows, cols), device="cuda", generator=gen)
+        chi = sum(torch.randn((rows, cols), device="cuda", generator=gen) ** 2 for _ in range(4)) / 4
+        w = (0.02 * z / chi.sqrt()).half()
+        del z, chi
+        g = torch.randn((rows, cols), device="cuda", generator=gen)
+        sens = (g * g).float()
+        del g
+        t = {}
+        for rep in range(3):                       # the first pass warms up; the last is kept
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            t_min, t_max, t_s, nnz = nw.outlier_thresholds(w, 2000, sens, 500)
+            t1 = time.perf_counter()
+            rp, col, val, dense, sdense = nw.outlier_extract(w, t_min, t_max, nnz, sens, t_s)
+            t2 = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            codes, lut = nw.kmeans_lut(dense, 3, 20, sdense)
+            e1.record()
+            torch.cuda.synchronize()
+            t = {"thresholds_ms": (t1 - t0) * 1e3, "extract_ms": (t2 - t1) * 1e3,
+                 "kmeans_ms": e0.elapsed_time(e1)}
+        total = sum(t.values())
+        layer_ms += count * total
+        r = {"shape": f"{rows}x{cols}", "per_layer": count, "nnz": nnz, "density_pct": round(100 * nnz / (rows * cols), 4),
+             **{k: round(v, 3) for k, v in t.items()}, "total_ms": round(total, 3),
+             "kmeans_weight_steps_per_s": round(rows * cols * 20 / (t["kmeans_ms"] * 1e-3) / 1e9, 1)}
+        log(f"offline {r}")
+        res.append(r)
+        if rows == cols:
+            sample = (w[:512].cpu(), sens[:512].cpu(), dense[:8].cpu(), sdense[:8].cpu(), rows)
+        del w, sens, rp, col, val, dense, sdense, codes, lut
+        torch.cuda.empty_cache()
+    out = {"ablation": "offline", "workload": "LLaMA-65B layer: 8192x8192 x4, 22016x8192 x2, 8192x22016 x1; "
+           "0.4% outliers + 0.05% sensitive values; 3-bit weighted k-means, 20 steps", "shapes": res,
+           "layer_ms": round(layer_ms, 2), "model_80_layers_s": round(80 * layer_ms / 1e3, 2)}
+    if not args.no_cpu_baseline:
+        from oracle import quantize as q
+        w_s, s_s, d_s, sd_s, rows = sample
+        wb = w_s.view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        t_min, t_max, t_s, _ = q.split_thresholds(wb, 2000, s_s.numpy(), 500)
+        q.extract(wb, t_min, t_max, s_s.numpy(), t_s)
+        t1 = time.perf_counter()
+        q.kmeans_lut(d_s.view(torch.int16).numpy().view(np.uint16), sd_s.numpy(), 3, 20)
+        t2 = time.perf_counter()
+        split_ms = (t1 - t0) * 1e3 * rows / 512
+        km_ms = (t2 - t1) * 1e3 * rows / 8
+        out["cpu_baseline"] = {"kind": "oracle", "cores": 1, "unit": "ms per 8192x8192 matrix",
+                               "split_ms": round(split_ms, 1), "kmeans_ms": round(km_ms, 1),
+                               "sample": "split of rows 0-511 (thresholds over the slice) and k-means of rows 0-7, "
+                                         "scaled by rows"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.ablation == "outliers":
@@ -369,8 +445,11 @@ def main():
     if args.ablation == "batch":
         batch_ablation(args)
         return
+    if args.ablation == "offline":
+        offline_ablation(args)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the design notes describe row sharding across GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
