@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--ablation", choices=("outliers", "batch", "offline"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
-                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8; offline: the "
+                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8 in both dense forms; offline: the "
                         "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
@@ -307,7 +307,8 @@ def outlier_ablation(args) -> None:
 
 
 def batch_ablation(args) -> None:
-    """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4 and 8:
+    """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4 and 8,
+    batches 2..8 in both dense forms (matrix-core, the default, and v_dot2c):
     µs per product and effective GB/s (bytes grow only by x and y, the math by
     the batch), graph-timed over copies of the inputs (>= 1.2 GB)."""
     import numpy as np
@@ -319,7 +320,8 @@ def batch_ablation(args) -> None:
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     out = []
-    for batch in (1, 2, 4, 8):
+    for batch, form in [(1, "dot"), (2, "matrix"), (2, "dot"), (4, "matrix"), (4, "dot"), (8, "matrix"), (8, "dot")]:
+        nw.set_tuning(dot_only=1 if form == "dot" and batch > 1 else 0)
         for i, spec in enumerate(synth.workload(4, batch=batch)):
             m = synth.make_matrix(spec, seed=args.seed, workload=4, index=i)
             packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
@@ -352,12 +354,13 @@ def batch_ablation(args) -> None:
                 torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / 200 * 1e3
             nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, int(m.col.size), batch)
-            res = {"batch": batch, "shape": f"{spec.rows}x{spec.cols}", "us": round(us, 3),
+            res = {"batch": batch, "form": form, "shape": f"{spec.rows}x{spec.cols}", "us": round(us, 3),
                    "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
             log(f"batch ablation {res}")
             out.append(res)
             del copies, packed, lut, rp, col, val
             torch.cuda.empty_cache()
+    nw.set_tuning()
     print(json.dumps({"ablation": "batch", "unit": "us per product and effective GB/s", "products": out}),
           flush=True)
 

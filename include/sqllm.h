@@ -75,8 +75,13 @@
  * call therefore leaves it ready for the next one, so one workspace serves
  * any sequence of calls, of any shapes it is large enough for, that are
  * ordered on one stream.  Calls that may run concurrently need separate
- * workspaces.  When a call does not split (small shapes) the workspace may
- * be NULL.  Results are bit-identical run to run whenever a row's columns
+ * workspaces.  At batch >= 5 the workspace also holds, behind the words, a
+ * transposed copy of x ([cols][8] fp16) from which the outliers
+ * read all batch columns of a column in one load; the call writes it before
+ * its product kernel and clears it after, so the whole workspace is zero
+ * again when the call's work on the stream is done.  When a call does not split (small shapes) the workspace may be
+ * NULL, or smaller than sqllm_workspace_bytes() but at least the words: the
+ * outliers then read x in place.  Results are bit-identical run to run whenever a row's columns
  * are split over at most two workgroups (all shapes up to 22016 x 22016 with
  * the built-in launch shapes); beyond that the fp32 partial sums are added
  * in arrival order.
@@ -114,8 +119,9 @@ const char *sqllm_status_string(sqllm_status s);
 size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits);
 
 /* Bytes of workspace the hot calls need for this shape and batch (the same
- * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv);
- * 0 if the arguments are out of range. */
+ * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv):
+ * ceil(rows / 64) * 64 * batch * 8, plus at batch >= 5 the transposed x,
+ * cols * 16 rounded up to 256; 0 if the arguments are out of range. */
 size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch);
 
 /*
@@ -290,11 +296,13 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
  *   SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES, else built in).  sparse_naive
  *   = 1 switches the outliers to the unbalanced form for the ablation of the
  *   balanced kernel (summary page, Appendix C, Table C.1): one thread per
- *   row walks the row's nonzeros; 0 restores the balanced form.  Shapes that no
- *   compiled kernel fits fail with SQLLM_ERR_SHAPE.  Results agree within the
- *   stated tolerance for every shape; not thread-safe against concurrent
- *   calls. */
-sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive);
+ *   row walks the row's nonzeros; 0 restores the balanced form.  dot_only =
+ *   1 keeps the dense part in the v_dot2c form at batch >= 2 (for the
+ *   comparison with the matrix-core form those batches use by default); 0
+ *   restores the default.  Shapes that no compiled kernel fits fail with
+ *   SQLLM_ERR_SHAPE.  Results agree within the stated tolerance for every
+ *   shape; not thread-safe against concurrent calls. */
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive, int dot_only);
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
                                uint16_t *w, hipStream_t stream);
 

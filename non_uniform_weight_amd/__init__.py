@@ -69,7 +69,7 @@ _lib.sqllm_kmeans_lut.argtypes = [_vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _v
 _lib.sqllm_test_unpack.restype = _i32
 _lib.sqllm_test_unpack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
 _lib.sqllm_test_tuning.restype = _i32
-_lib.sqllm_test_tuning.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.sqllm_test_tuning.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 _lib.sqllm_test_decode.restype = _i32
 _lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
 
@@ -324,10 +324,11 @@ def decode_weights(packed, lut, rows, cols, bits, stream=None) -> torch.Tensor:
 
 
 def set_tuning(target_wgs: int = 0, min_gps: int = 0, split: int = 0, waves: int = 0,
-               sparse_naive: int = 0) -> None:
+               sparse_naive: int = 0, dot_only: int = 0) -> None:
     """Test-only: launch shape of later calls (0 = default); sparse_naive=1 selects the unbalanced
-    one-thread-per-row outlier form (ablation)."""
-    _check(_lib.sqllm_test_tuning(target_wgs, min_gps, split, waves, sparse_naive), "sqllm_test_tuning")
+    one-thread-per-row outlier form, dot_only=1 the v_dot2c dense form at every batch (ablations)."""
+    _check(_lib.sqllm_test_tuning(target_wgs, min_gps, split, waves, sparse_naive, dot_only),
+           "sqllm_test_tuning")
 
 
 def algorithmic_bytes(rows: int, cols: int, bits: int, nnz: int, batch: int) -> int:

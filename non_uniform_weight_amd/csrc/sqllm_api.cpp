@@ -22,6 +22,7 @@ struct Tuning {
     int force_split = 0;    // 0: choose; else workgroups per row tile
     int force_waves = 0;    // 0: choose; else waves per workgroup
     int sparse_naive = 0;   // ablation: 1 = outliers one lane per row, unbalanced
+    int dot_only = 0;       // ablation: 1 = dense part in the dot form at every batch
     Tuning()
     {
         auto get = [](const char *name, int lo, int hi, int dflt) {
@@ -57,11 +58,19 @@ sqllm_status check_shape(int64_t rows, int64_t cols)
     return SQLLM_OK;
 }
 
-// One 8-byte (fp32 sum, count) word per (tile, batch column, row of tile).
-size_t workspace_need(int64_t rows, int batch)
+// One 8-byte (fp32 sum, count) word per (tile, batch column, row of tile),
+// then (batch >= 2) x transposed for the outlier gathers.
+size_t slots_need(int64_t rows, int batch)
 {
     return (size_t)tiles_of(rows) * (size_t)batch * kTileRows * 8;
 }
+
+size_t workspace_need(int64_t rows, int64_t cols, int batch) { return slots_need(rows, batch) + xt_bytes(cols, batch); }
+
+// Outliers at batch >= kXtBatch whose x is not staged in LDS gather from a
+// transposed copy in the workspace (when the workspace has room for it):
+// one load per nonzero instead of one per batch column.
+bool wants_xt(const KernelArgs &a, int batch, int64_t nnz) { return batch >= kXtBatch && nnz > 0 && !a.x_lds; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -96,6 +105,10 @@ int choose_waves(int64_t workgroups)
     return workgroups > tuning().target_wgs ? kDefaultWaves : kMaxWaves;
 }
 
+// Dense part on the matrix cores from batch 2 on: the dot form's v_dot2c
+// count grows with the batch, one 4x4x4 matrix step covers 4 batch columns.
+int use_mf(int batch) { return batch >= 2 && !tuning().dot_only ? 1 : 0; }
+
 // Stage x in LDS for the outlier gathers when it fits beside the pair table
 // (in half of the LDS when two workgroups share a unit).
 void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int waves, LaunchShape &ls)
@@ -113,6 +126,7 @@ void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int waves, LaunchShape 
 void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
 {
     choose_split(a, a.tiles);
+    ls.mf = use_mf(batch);
     ls.waves = choose_waves((int64_t)a.tiles * a.split);
     ls.dyn_lds = 0;
     choose_x_lds(a, batch, nnz, ls.waves, ls);
@@ -163,8 +177,33 @@ sqllm_status sparse_checks(const int32_t *row_ptr, const uint16_t *col_idx, cons
 sqllm_status workspace_checks(int split, int64_t rows, int batch, void *ws, size_t ws_bytes)
 {
     if (split <= 1) return SQLLM_OK;
-    if (!ws || !aligned(ws, 256) || ws_bytes < workspace_need(rows, batch)) return SQLLM_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256) || ws_bytes < slots_need(rows, batch)) return SQLLM_ERR_WORKSPACE;
     return SQLLM_OK;
+}
+
+// Sets a.xt when the outliers want a transposed x, the products reading
+// that x carry at least kXtMinNnz nonzeros (nnz_x) and the workspace holds
+// it; products with the same x share one copy.  The copy is written before
+// the product launch and cleared after it, so the workspace is all zero
+// again between calls (any later call may use those bytes as its words).
+void plan_xt(KernelArgs &a, int batch, int64_t nnz, int64_t nnz_x, void *ws, size_t ws_bytes, XtJobs &jobs)
+{
+    a.xt = nullptr;
+    if (!wants_xt(a, batch, nnz) || nnz_x < kXtMinNnz || !ws || !aligned(ws, 256) ||
+        ws_bytes < workspace_need(a.rows, a.cols, batch))
+        return;
+    for (int k = 0; k < jobs.n; ++k)
+        if (jobs.x[k] == a.x && jobs.cols[k] == a.cols) {
+            a.xt = jobs.xt[k];
+            return;
+        }
+    uint16_t *xt = (uint16_t *)((char *)ws + slots_need(a.rows, batch));
+    jobs.x[jobs.n] = a.x;
+    jobs.xt[jobs.n] = xt;
+    jobs.cols[jobs.n] = a.cols;
+    if (a.cols > jobs.max_cols) jobs.max_cols = a.cols;
+    ++jobs.n;
+    a.xt = xt;
 }
 
 KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y, void *ws)
@@ -211,7 +250,7 @@ size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits)
 size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch)
 {
     if (check_shape(rows, cols) != SQLLM_OK || batch < 1 || batch > kMaxBatch) return 0;
-    return workspace_need(rows, batch);
+    return workspace_need(rows, cols, batch);
 }
 
 sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed, hipStream_t stream)
@@ -264,7 +303,11 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     choose_dense(a, batch, nnz, ls);
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
-    if (launch_dense_sparse(a, bits, batch, nnz > 0 ? kFused : kDenseOnly, ls, stream) != hipSuccess)
+    XtJobs jobs{};
+    plan_xt(a, batch, nnz, nnz, workspace, workspace_bytes, jobs);
+    if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
+        launch_dense_sparse(a, bits, batch, nnz > 0 ? kFused : kDenseOnly, ls, stream) != hipSuccess ||
+        launch_xt_clear(jobs, batch, stream) != hipSuccess)
         return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }
@@ -287,7 +330,12 @@ sqllm_status sqllm_spmv_add(const int32_t *row_ptr, const uint16_t *col_idx, con
     choose_sparse(a, batch, nnz, ls);
     st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
     if (st != SQLLM_OK) return st;
-    if (launch_dense_sparse(a, 3, batch, kSparseAdd, ls, stream) != hipSuccess) return SQLLM_ERR_HIP;
+    XtJobs jobs{};
+    plan_xt(a, batch, nnz, nnz, workspace, workspace_bytes, jobs);
+    if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
+        launch_dense_sparse(a, 3, batch, kSparseAdd, ls, stream) != hipSuccess ||
+        launch_xt_clear(jobs, batch, stream) != hipSuccess)
+        return SQLLM_ERR_HIP;
     return SQLLM_OK;
 }
 
@@ -297,7 +345,7 @@ size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch)
     size_t total = 0;
     for (int i = 0; i < n; ++i) {
         if (check_shape(items[i].rows, items[i].cols) != SQLLM_OK) return 0;
-        total += workspace_need(items[i].rows, batch);
+        total += workspace_need(items[i].rows, items[i].cols, batch);
     }
     return total;
 }
@@ -330,15 +378,19 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
         if (total_tiles == 0) continue;
         size_t ws_off = 0;
         int64_t wgs = 0;
+        void *own_ws[kMaxGroup];   // each product's workspace region (slots, then transposed x) or null
+        size_t own_bytes[kMaxGroup];
+        int64_t own_nnz[kMaxGroup];
         for (int i = 0; i < n; ++i) {
             const sqllm_product &p = items[i];
-            const size_t need = workspace_need(p.rows, batch); // every product has its own slots
+            const size_t need = workspace_need(p.rows, p.cols, batch); // every product has its own region
             if ((p.nnz > 0) != fused) {
                 ws_off += need;
                 continue;
             }
-            KernelArgs a = base_args(p.rows, p.cols, p.x, p.y,
-                                     workspace ? (void *)((char *)workspace + ws_off) : nullptr);
+            void *mine = workspace ? (void *)((char *)workspace + ws_off) : nullptr;
+            const size_t left = workspace && workspace_bytes > ws_off ? workspace_bytes - ws_off : 0;
+            KernelArgs a = base_args(p.rows, p.cols, p.x, p.y, mine);
             ws_off += need;
             a.packed = p.packed;
             a.lut = p.lut;
@@ -346,7 +398,10 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
             a.col = p.col_idx;
             a.val = p.val;
             choose_split(a, total_tiles);
-            if (a.split > 1 && (!workspace || workspace_bytes < ws_off)) return SQLLM_ERR_WORKSPACE;
+            if (a.split > 1 && (!workspace || left < slots_need(p.rows, batch))) return SQLLM_ERR_WORKSPACE;
+            own_ws[g.n] = mine;
+            own_bytes[g.n] = left < need ? left : need;
+            own_nnz[g.n] = p.nnz;
             g.item[g.n] = a;
             if ((int64_t)a.tiles * a.split > g.wgs) g.wgs = a.tiles * a.split;
             wgs += (int64_t)a.tiles * a.split;
@@ -354,9 +409,20 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
         }
         if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
         LaunchShape ls{};
+        ls.mf = use_mf(batch);
         ls.waves = choose_waves(wgs);
+        XtJobs jobs{}; // products that share x (as q, k and v do) share one transposed copy
         for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);
-        if (launch_dense_sparse_group(g, bits, batch, fused ? kFused : kDenseOnly, ls, stream) != hipSuccess)
+        for (int k = 0; k < g.n; ++k) {
+            int64_t nnz_x = 0; // nonzeros of this launch's products that gather from the same x
+            for (int j = 0; j < g.n; ++j)
+                if (g.item[j].x == g.item[k].x && g.item[j].cols == g.item[k].cols && !g.item[j].x_lds)
+                    nnz_x += own_nnz[j];
+            plan_xt(g.item[k], batch, fused ? 1 : 0, nnz_x, own_ws[k], own_bytes[k], jobs);
+        }
+        if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
+            launch_dense_sparse_group(g, bits, batch, fused ? kFused : kDenseOnly, ls, stream) != hipSuccess ||
+            launch_xt_clear(jobs, batch, stream) != hipSuccess)
             return SQLLM_ERR_HIP;
     }
     return SQLLM_OK;
@@ -483,16 +549,19 @@ sqllm_status sqllm_kmeans_lut(const uint16_t *dense, const float *sens, int64_t 
     return SQLLM_OK;
 }
 
-sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive)
+sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive, int dot_only)
 {
     const Tuning dflt;
-    if (split > kMaxSplit || waves > kMaxWaves || sparse_naive < 0 || sparse_naive > 1) return SQLLM_ERR_SHAPE;
+    if (split > kMaxSplit || waves > kMaxWaves || sparse_naive < 0 || sparse_naive > 1 || dot_only < 0 ||
+        dot_only > 1)
+        return SQLLM_ERR_SHAPE;
     Tuning &t = tuning_state();
     t.target_wgs = target_wgs > 0 ? target_wgs : dflt.target_wgs;
     t.min_gps = min_gps > 0 ? min_gps : dflt.min_gps;
     t.force_split = split > 0 ? split : dflt.force_split;
     t.force_waves = waves > 0 ? waves : dflt.force_waves;
     t.sparse_naive = sparse_naive;
+    t.dot_only = dot_only;
     return SQLLM_OK;
 }
 

@@ -53,6 +53,9 @@ namespace sqllm {
 namespace dev {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Zeros read by the ring's placeholder loads: a wave always issues the same
@@ -115,28 +118,32 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
     }
 }
 
-// Registers of one group in flight: codes, and the group's activations
-// (xr[b][0..3] = pairs 4n..4n+3, xr[b][4..7] = pairs 64+4n..64+4n+3 with
-// n = lane % 16, for batch column b).
-template <int BITS, int B>
+// Registers of one group in flight: codes, and the group's activations.
+// Dot form: xr[b][0..3] = pairs 4n..4n+3, xr[b][4..7] = pairs 64+4n..64+4n+3
+// with n = lane % 16, for batch column b.  Matrix-core form (MF): lane 4k+i
+// holds in xq[2h + s] the 8 activations of batch column 4h+i at columns
+// 128 s + 8 k .. 128 s + 8 k + 7 of the group.
+template <int BITS, int B, bool MF>
 struct GroupRegs {
     uint32_t d[Format<BITS>::kDwords];
-    uint32_t xr[B][8];
+    uint32_t xr[MF ? 1 : B][8];
+    u32x4 xq[MF ? 2 * mf_quads(B) : 1];
 };
 
-// Groups a dense wave keeps in flight, sized so the ring stays within 64
+// Groups a dense wave keeps in flight, sized so the ring stays within 80
 // (3-bit) or 72 (4-bit, whose table items and lookups need more) of the 128
-// registers a wave has when 16 waves share a compute unit.
-constexpr int ring_depth(int bits, int batch)
+// registers a wave has when 16 waves share a compute unit, less 16 per batch
+// quad in the matrix-core form (its accumulators).
+constexpr int ring_depth(int bits, int batch, bool mf)
 {
-    const int per = 8 * bits + 8 * batch;
-    const int d = (bits == 3 ? 80 : 72) / per;
+    const int per = 8 * bits + (mf ? 8 * mf_quads(batch) : 8 * batch);
+    const int d = ((bits == 3 ? 80 : 72) - (mf ? 16 * mf_quads(batch) : 0)) / per;
     return d < 1 ? 1 : (d > 3 ? 3 : d);
 }
 
 // Loads of group g of tile t into r; g < 0 loads placeholders.
-template <int BITS, int B>
-__device__ __forceinline__ void load_group(GroupRegs<BITS, B> &r, const KernelArgs &a, int t, int g, int lane)
+template <int BITS, int B, bool MF>
+__device__ __forceinline__ void load_group(GroupRegs<BITS, B, MF> &r, const KernelArgs &a, int t, int g, int lane)
 {
     constexpr int NP = Format<BITS>::kPieces;
     const bool real = g >= 0;
@@ -150,6 +157,20 @@ __device__ __forceinline__ void load_group(GroupRegs<BITS, B> &r, const KernelAr
         r.d[4 * q + 1] = v.y;
         r.d[4 * q + 2] = v.z;
         r.d[4 * q + 3] = v.w;
+    }
+    if constexpr (MF) {
+#pragma unroll
+        for (int h = 0; h < mf_quads(B); ++h) {
+            const int b = 4 * h + (lane & 3); // batch columns past B read placeholders (their sums are dropped)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const u32x4 *xs = real && b < B
+                                      ? (const u32x4 *)(a.x + (int64_t)b * a.cols + g * 256 + 128 * s + 8 * (lane >> 2))
+                                      : (const u32x4 *)g_placeholder + lane;
+                r.xq[2 * h + s] = *xs;
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -179,8 +200,8 @@ constexpr int acc_chains(int batch) { return batch == 1 ? 3 : (batch == 2 ? 2 : 
 // (instead of one per read) covers them.
 constexpr int kBatch = 8;
 
-template <int BITS, int B, int Q>
-__device__ __forceinline__ void batch_reads(const GroupRegs<BITS, B> &r, uint32_t lane4, const uint32_t *tab,
+template <int BITS, int B, bool MF, int Q>
+__device__ __forceinline__ void batch_reads(const GroupRegs<BITS, B, MF> &r, uint32_t lane4, const uint32_t *tab,
                                             uint32_t (&wv)[kBatch])
 {
     uint32_t addr[kBatch];
@@ -327,7 +348,7 @@ struct PairDots<8, N> {
 
 // acc[b * acc_chains(B) + chain]
 template <int BITS, int B, int Q>
-__device__ __forceinline__ void batch_macs(const GroupRegs<BITS, B> &r, const uint32_t (&wv)[kBatch], float *acc)
+__device__ __forceinline__ void batch_macs(const GroupRegs<BITS, B, false> &r, const uint32_t (&wv)[kBatch], float *acc)
 {
     constexpr int h = Q / 8, n0 = 2 * (Q % 8);
     if constexpr (B <= 2) {
@@ -353,22 +374,70 @@ __device__ __forceinline__ void batch_macs(const GroupRegs<BITS, B> &r, const ui
 
 // All 128 pairs (256 codes) of one group.
 template <int BITS, int B>
-__device__ __forceinline__ void mac_group(const GroupRegs<BITS, B> &r, uint32_t lane4, const uint32_t *tab,
+__device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, false> &r, uint32_t lane4, const uint32_t *tab,
                                           float *acc)
 {
     constexpr int NQ = 128 / kBatch;
     uint32_t wv[2][kBatch];
-    batch_reads<BITS, B, 0>(r, lane4, tab, wv[0]);
+    batch_reads<BITS, B, false, 0>(r, lane4, tab, wv[0]);
     [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
         (
             [&] {
-                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
+                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, false, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
                 // one wait for the whole batch: the empty statement needs all
                 // eight table reads of batch Qs
                 const uint32_t(&cur)[kBatch] = wv[Qs & 1];
                 asm volatile("" ::"v"(cur[0]), "v"(cur[1]), "v"(cur[2]), "v"(cur[3]), "v"(cur[4]), "v"(cur[5]),
                              "v"(cur[6]), "v"(cur[7]));
                 batch_macs<BITS, B, Qs>(r, cur, acc);
+            }(),
+            ...);
+    }(std::make_integer_sequence<int, NQ>{});
+}
+
+// Matrix-core form: v_mfma_f32_4x4x4f16 in its 16-block shape.  Block q of
+// the instruction is lanes 4q..4q+3: lane 4q+i gives row i of the block's A
+// (4 x 4), lane 4q+j gives column j of its B (4 x 4), and register i of lane
+// 4q+j receives D[i][j].  With CBSZ = 4 every block takes the A of block
+// ABID instead of its own.  Here B is the lane's own row (lane = row of the
+// tile: two table entries, 4 consecutive weights) and A the 4 activations of
+// batch columns 4h..4h+3 at those columns, broadcast from the block that
+// holds them: register i of lane r ends with row r's sum for batch column
+// 4h+i.  No activation passes through LDS; the 16 blocks each hold a
+// different 8 columns of x, so one 16-byte register per 128 columns and
+// batch quad serves every step.
+// Step m (columns 4m .. 4m + 3 of the group) of every batch quad; cw holds
+// the table entries of the step's batch of 8 pairs.
+template <int BITS, int B, int M>
+__device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const uint32_t (&cw)[kBatch],
+                                        f32x4 (&macc)[mf_quads(B)][2])
+{
+    constexpr int S = M % 4, sx = M / 32, blk = (M % 32) / 2, part = M % 2;
+    const half4_t bv = __builtin_bit_cast(half4_t, u32x2{cw[2 * S], cw[2 * S + 1]});
+#pragma unroll
+    for (int h = 0; h < mf_quads(B); ++h) {
+        const u32x4 xq = r.xq[2 * h + sx];
+        const half4_t av = __builtin_bit_cast(half4_t, part ? u32x2{xq.z, xq.w} : u32x2{xq.x, xq.y});
+        macc[h][S & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, macc[h][S & 1], 4, blk, 0);
+    }
+}
+
+template <int BITS, int B>
+__device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, true> &r, uint32_t lane4, const uint32_t *tab,
+                                          f32x4 (&macc)[mf_quads(B)][2])
+{
+    constexpr int NQ = 128 / kBatch; // 16 batches of 8 pairs (16 columns, 4 steps of 4)
+    uint32_t wv[2][kBatch];
+    batch_reads<BITS, B, true, 0>(r, lane4, tab, wv[0]);
+    [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
+        (
+            [&] {
+                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, true, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
+                const uint32_t(&cw)[kBatch] = wv[Qs & 1];
+                mf_step<BITS, B, 4 * Qs + 0>(r, cw, macc);
+                mf_step<BITS, B, 4 * Qs + 1>(r, cw, macc);
+                mf_step<BITS, B, 4 * Qs + 2>(r, cw, macc);
+                mf_step<BITS, B, 4 * Qs + 3>(r, cw, macc);
             }(),
             ...);
     }(std::make_integer_sequence<int, NQ>{});
@@ -492,17 +561,49 @@ __device__ __forceinline__ float row_bcast31(float v)
 // broadcasts) gives every run's sum as the difference of two prefix values,
 // which each row lane fetches from the run's last lane and the lane before
 // its first.
-template <int B, int NC, bool XL>
-__device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int cb, int v1, const KernelArgs &a, int lane,
-                                             int rp_lo, int rp_hi, const uint16_t *xl, float *acc)
+// The activations of this lane's nonzero (column colv) for every batch column.
+template <int B, bool XL>
+__device__ __forceinline__ void sparse_gather(uint32_t colv, const KernelArgs &a, const uint16_t *xl, uint16_t (&xv)[B])
+{
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const int64_t xi = (int64_t)b * a.cols + (int)colv;
+        xv[b] = XL ? xl[xi] : a.x[xi];
+    }
+}
+
+// The same from the transposed copy: one load, one cache line per lane.
+template <int B>
+__device__ __forceinline__ void sparse_gather_t(uint32_t colv, const uint16_t *xt, uint16_t (&xv)[B])
+{
+    constexpr int P = xt_pad(B);
+    uint32_t w[P / 2];
+    if constexpr (P == 2) {
+        w[0] = *(const uint32_t *)(xt + (int64_t)colv * 2);
+    } else if constexpr (P == 4) {
+        const u32x2 v = *(const u32x2 *)(xt + (int64_t)colv * 4);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        const u32x4 v = *(const u32x4 *)(xt + (int64_t)colv * 8);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) xv[b] = (uint16_t)(w[b >> 1] >> (16 * (b & 1)));
+}
+
+template <int B, int NC>
+__device__ __forceinline__ void sparse_scan(uint32_t valv, const uint16_t (&xv)[B], int cb, int v1, int lane, int rp_lo,
+                                            int rp_hi, float *acc)
 {
     const float vv = cb + lane < v1 ? f16_to_f32((uint16_t)valv) : 0.f;
-    const int col = (int)colv;
     float pre[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const int64_t xi = (int64_t)b * a.cols + col;
-        float v = vv * f16_to_f32(XL ? xl[xi] : a.x[xi]);
+        float v = vv * f16_to_f32(xv[b]);
         v += row_shr<1>(v);
         v += row_shr<2>(v);
         v += row_shr<4>(v);
@@ -522,6 +623,15 @@ __device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int c
         const float below = lane_read(e_lo, pre[b]);
         if (present) acc[b * NC] += first > 0 ? top - below : top;
     }
+}
+
+template <int B, int NC, bool XL>
+__device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int cb, int v1, const KernelArgs &a, int lane,
+                                             int rp_lo, int rp_hi, const uint16_t *xl, float *acc)
+{
+    uint16_t xv[B];
+    sparse_gather<B, XL>(colv, a, xl, xv);
+    sparse_scan<B, NC>(valv, xv, cb, v1, lane, rp_lo, rp_hi, acc);
 }
 
 // Issue the first ring of code loads only after the pair table is built:
@@ -596,18 +706,19 @@ __device__ __forceinline__ void load_args_now(const KernelArgs &a)
 {
     asm volatile("" ::"s"(a.packed), "s"(a.lut), "s"(a.row_ptr), "s"(a.col), "s"(a.val), "s"(a.x), "s"(a.y),
                  "s"(a.slots), "s"(a.rows), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
-                 "s"(a.x_lds), "s"(a.sparse_naive), "s"(blockDim.x));
+                 "s"(a.x_lds), "s"(a.xt), "s"(a.sparse_naive), "s"(blockDim.x));
 }
 
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool MF>
 __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 {
     load_args_now(a);
     constexpr bool DENSE = MODE != kSparseAdd;
     constexpr bool SPARSE = MODE != kDenseOnly;
     constexpr bool ADDY = MODE == kSparseAdd;
+    static_assert(!MF || (DENSE && B >= 2), "matrix-core form: dense modes, batch >= 2");
     constexpr int E = Format<BITS>::kEntries;
-    constexpr int D = ring_depth(BITS, B);
+    constexpr int D = ring_depth(BITS, B, MF);
     constexpr int ITEMS = DENSE ? (64 * E) / 512 : 1; // table items per thread with 8 waves
     __shared__ __align__(16) uint32_t tab[DENSE ? kTableBytes / 4 : kMaxWaves * B * 64];
     extern __shared__ __align__(16) uint32_t dyn[];
@@ -620,10 +731,15 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     const int row0 = t * 64;
     const uint32_t lane4 = (uint32_t)lane << 2;
 
-    constexpr int NC = acc_chains(B);
-    float acc[B * NC]; // dense chains; outliers add into chain 0
+    constexpr int NC = MF ? 1 : acc_chains(B);
+    float acc[B * NC]; // dense chains (dot form); outliers add into chain 0
 #pragma unroll
     for (int k = 0; k < B * NC; ++k) acc[k] = 0.f;
+    constexpr int NX = MF ? mf_quads(B) : 1;
+    f32x4 macc[NX][2]; // matrix-core form: [batch quad][chain]
+#pragma unroll
+    for (int h = 0; h < NX; ++h) macc[h][0] = macc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t *xstage = dyn; // dynamic LDS: x staged for the outlier gathers
 
     // -- 1. the pair-table items beyond ITEMS per thread (workgroups of fewer
     //       than 8 waves only)
@@ -661,12 +777,18 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     const int gb = s * a.gps;
     const int ge = min(gb + a.gps, a.groups);
     const int cnt = DENSE ? max(0, (ge - gb - w + W - 1) / W) : 0; // this wave's groups
-    GroupRegs<BITS, B> ring[DENSE ? D : 1];
+    GroupRegs<BITS, B, MF> ring[DENSE ? D : 1];
     auto issue_ring = [&]() {
         if constexpr (DENSE) {
 #pragma unroll
-            for (int k = 0; k < D; ++k) load_group<BITS, B>(ring[k], a, t, k < cnt ? gb + w + k * W : -1, lane);
+            for (int k = 0; k < D; ++k) load_group<BITS, B, MF>(ring[k], a, t, k < cnt ? gb + w + k * W : -1, lane);
         }
+    };
+    auto dense_math = [&](const GroupRegs<BITS, B, MF> &r) {
+        if constexpr (MF)
+            mac_group<BITS, B>(r, lane4, tab, macc);
+        else
+            mac_group<BITS, B>(r, lane4, tab, acc);
     };
     if constexpr (!kRingAfterTable) issue_ring();
 
@@ -699,8 +821,8 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     if constexpr (SPARSE) {
 #pragma unroll
         for (int k = 0; k < kStageQuads; ++k)
-            if ((int)threadIdx.x + k * nt < nxq) ((u32x4 *)dyn)[threadIdx.x + k * nt] = xq[k];
-        for (int i = threadIdx.x + kStageQuads * nt; i < nxq; i += nt) ((u32x4 *)dyn)[i] = ((const u32x4 *)a.x)[i];
+            if ((int)threadIdx.x + k * nt < nxq) ((u32x4 *)xstage)[threadIdx.x + k * nt] = xq[k];
+        for (int i = threadIdx.x + kStageQuads * nt; i < nxq; i += nt) ((u32x4 *)xstage)[i] = ((const u32x4 *)a.x)[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (kRingAfterTable) issue_ring();
@@ -708,7 +830,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     // -- 6. dense steps: a main loop in which every step refills the ring,
     //       then the last (fewer than 2D) groups, each of those followed by
     //       one chunk of the first round of nonzeros
-    const uint16_t *xl = (const uint16_t *)dyn;
+    const uint16_t *xl = (const uint16_t *)xstage;
     const int r0end = min(v1, v0 + 64 * R);
     auto chunk = [&](auto kc) { // chunk K of the first round, if the share has it
         constexpr int K = decltype(kc)::value;
@@ -728,8 +850,8 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         for (; j0 + 2 * D <= cnt; j0 += D) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
-                mac_group<BITS, B>(ring[k], lane4, tab, acc);
-                load_group<BITS, B>(ring[k], a, t, gb + w + (j0 + k + D) * W, lane);
+                dense_math(ring[k]);
+                load_group<BITS, B, MF>(ring[k], a, t, gb + w + (j0 + k + D) * W, lane);
             }
         }
         [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
@@ -738,8 +860,8 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
                     constexpr int k = Ks;
                     const int j = j0 + k;
                     if (j < cnt) {
-                        mac_group<BITS, B>(ring[k], lane4, tab, acc);
-                        if (j + D < cnt) load_group<BITS, B>(ring[k], a, t, gb + w + (j + D) * W, lane);
+                        dense_math(ring[k]);
+                        if (j + D < cnt) load_group<BITS, B, MF>(ring[k], a, t, gb + w + (j + D) * W, lane);
                         if (a.x_lds) {
                             chunk(std::integral_constant<int, k>{});
                             done = k + 1;
@@ -751,7 +873,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
                 [&] {
                     constexpr int k = Ks;
                     if (j0 + D + k < cnt) {
-                        mac_group<BITS, B>(ring[k], lane4, tab, acc);
+                        dense_math(ring[k]);
                         if (a.x_lds) {
                             chunk(std::integral_constant<int, D + k>{});
                             done = D + k + 1;
@@ -777,33 +899,47 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
                 }
             }
         }
-        [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
-            ((Ks >= done ? chunk(std::integral_constant<int, Ks>{}) : void()), ...);
-        }(std::make_integer_sequence<int, R>{});
+        // the rest a round at a time: every gather of the round, then the
+        // scans, so that a round waits for memory once rather than per chunk
+        auto finish_round = [&](int base, int kfirst) {
+            uint16_t xg[R][B];
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (k >= kfirst && base + 64 * k < v1) {
+                    if (a.x_lds)
+                        sparse_gather<B, true>(cv.col[k], a, xl, xg[k]);
+                    else if (B >= kXtBatch && a.xt)
+                        sparse_gather_t<B>(cv.col[k], a.xt, xg[k]);
+                    else
+                        sparse_gather<B, false>(cv.col[k], a, xl, xg[k]);
+                }
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (k >= kfirst && base + 64 * k < v1)
+                    sparse_scan<B, NC>(cv.val[k], xg[k], base + 64 * k, v1, lane, rp_lo, rp_hi, acc);
+        };
+        finish_round(v0, done);
         for (int base = v0 + 64 * R; base < v1; base += 64 * R) {
             sparse_round_load(cv, a, base, v1, lane);
-#pragma unroll
-            for (int k = 0; k < R; ++k) {
-                if (base + 64 * k >= v1) break;
-                if (a.x_lds)
-                    sparse_chunk<B, NC, true>(cv.col[k], cv.val[k], base + 64 * k, v1, a, lane, rp_lo, rp_hi, xl,
-                                              acc);
-                else
-                    sparse_chunk<B, NC, false>(cv.col[k], cv.val[k], base + 64 * k, v1, a, lane, rp_lo, rp_hi, xl,
-                                               acc);
-            }
+            finish_round(base, 0);
         }
     }
     lds_barrier(); // pair table no longer needed
 
     // -- 8. reduce the waves (fixed order), then round and store / hand over
     float *red = (float *)tab;
+    if constexpr (MF) {
+        // register i of the batch quad h: batch column 4h+i of this lane's row
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float v = acc[b * NC];
+        for (int b = 0; b < B; ++b) red[(w * B + b) * 64 + lane] = acc[b] + macc[b / 4][0][b % 4] + macc[b / 4][1][b % 4];
+    } else {
 #pragma unroll
-        for (int c = 1; c < NC; ++c) v += acc[b * NC + c];
-        red[(w * B + b) * 64 + lane] = v;
+        for (int b = 0; b < B; ++b) {
+            float v = acc[b * NC];
+#pragma unroll
+            for (int c = 1; c < NC; ++c) v += acc[b * NC + c];
+            red[(w * B + b) * 64 + lane] = v;
+        }
     }
     lds_barrier();
     if (w != 0) return;
@@ -817,10 +953,10 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     finish_rows<B, ADDY>(a, t, lane, tot, a.split);
 }
 
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool MF>
 __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs a)
 {
-    product_body<BITS, B, MODE>(a, blockIdx.x);
+    product_body<BITS, B, MODE, MF>(a, blockIdx.x);
 }
 
 // Several independent products in one launch: the workgroups of row y of the
@@ -829,19 +965,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
 // room, so one product's start-up (table rows, first code latency) and tail
 // (reductions) overlap the other products' code streams.  The product index
 // is blockIdx.y, so its arguments come in one round of scalar loads.
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool MF>
 __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(GroupArgs g)
 {
     const KernelArgs &a = g.item[blockIdx.y];
     load_args_now(a);
     if ((int)blockIdx.x >= a.tiles * a.split) return;
-    product_body<BITS, B, MODE>(a, blockIdx.x);
+    product_body<BITS, B, MODE, MF>(a, blockIdx.x);
 }
 
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool MF>
 hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
-    auto kern = dense_sparse_kernel<BITS, B, MODE>;
+    auto kern = dense_sparse_kernel<BITS, B, MODE, MF>;
     static bool attr_set = false; // ask once for more than the default dynamic LDS
     if (!attr_set) {
         const int static_lds = MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4;
@@ -856,10 +992,10 @@ hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t st
     return hipGetLastError();
 }
 
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool MF>
 hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
-    auto kern = dense_sparse_group_kernel<BITS, B, MODE>;
+    auto kern = dense_sparse_group_kernel<BITS, B, MODE, MF>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -873,18 +1009,36 @@ hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream
     return hipGetLastError();
 }
 
+// Batch 1 (and the sparse-only mode) in the dot form; batch >= 2 in the
+// matrix-core form when the shape asks for it.
+template <int BITS, int B, int MODE>
+hipError_t launch_group_form(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
+{
+    if constexpr (MODE != kSparseAdd && B >= 2)
+        if (ls.mf) return launch_group_one<BITS, B, MODE, true>(g, ls, stream);
+    return launch_group_one<BITS, B, MODE, false>(g, ls, stream);
+}
+
+template <int BITS, int B, int MODE>
+hipError_t launch_form(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
+{
+    if constexpr (MODE != kSparseAdd && B >= 2)
+        if (ls.mf) return launch_one<BITS, B, MODE, true>(a, ls, stream);
+    return launch_one<BITS, B, MODE, false>(a, ls, stream);
+}
+
 template <int BITS, int MODE>
 hipError_t launch_group_batch(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
 {
     switch (batch) {
-    case 1: return launch_group_one<BITS, 1, MODE>(g, ls, stream);
-    case 2: return launch_group_one<BITS, 2, MODE>(g, ls, stream);
-    case 3: return launch_group_one<BITS, 3, MODE>(g, ls, stream);
-    case 4: return launch_group_one<BITS, 4, MODE>(g, ls, stream);
-    case 5: return launch_group_one<BITS, 5, MODE>(g, ls, stream);
-    case 6: return launch_group_one<BITS, 6, MODE>(g, ls, stream);
-    case 7: return launch_group_one<BITS, 7, MODE>(g, ls, stream);
-    case 8: return launch_group_one<BITS, 8, MODE>(g, ls, stream);
+    case 1: return launch_group_form<BITS, 1, MODE>(g, ls, stream);
+    case 2: return launch_group_form<BITS, 2, MODE>(g, ls, stream);
+    case 3: return launch_group_form<BITS, 3, MODE>(g, ls, stream);
+    case 4: return launch_group_form<BITS, 4, MODE>(g, ls, stream);
+    case 5: return launch_group_form<BITS, 5, MODE>(g, ls, stream);
+    case 6: return launch_group_form<BITS, 6, MODE>(g, ls, stream);
+    case 7: return launch_group_form<BITS, 7, MODE>(g, ls, stream);
+    case 8: return launch_group_form<BITS, 8, MODE>(g, ls, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -893,14 +1047,14 @@ template <int BITS, int MODE>
 hipError_t launch_batch(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
     switch (batch) {
-    case 1: return launch_one<BITS, 1, MODE>(a, ls, stream);
-    case 2: return launch_one<BITS, 2, MODE>(a, ls, stream);
-    case 3: return launch_one<BITS, 3, MODE>(a, ls, stream);
-    case 4: return launch_one<BITS, 4, MODE>(a, ls, stream);
-    case 5: return launch_one<BITS, 5, MODE>(a, ls, stream);
-    case 6: return launch_one<BITS, 6, MODE>(a, ls, stream);
-    case 7: return launch_one<BITS, 7, MODE>(a, ls, stream);
-    case 8: return launch_one<BITS, 8, MODE>(a, ls, stream);
+    case 1: return launch_form<BITS, 1, MODE>(a, ls, stream);
+    case 2: return launch_form<BITS, 2, MODE>(a, ls, stream);
+    case 3: return launch_form<BITS, 3, MODE>(a, ls, stream);
+    case 4: return launch_form<BITS, 4, MODE>(a, ls, stream);
+    case 5: return launch_form<BITS, 5, MODE>(a, ls, stream);
+    case 6: return launch_form<BITS, 6, MODE>(a, ls, stream);
+    case 7: return launch_form<BITS, 7, MODE>(a, ls, stream);
+    case 8: return launch_form<BITS, 8, MODE>(a, ls, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -34,6 +34,7 @@ struct KernelArgs {
     int split;                // workgroups per row tile
     int gps;                  // column groups per workgroup (the last one may have fewer)
     int x_lds;                // 1: all of x staged in LDS for the outlier gathers
+    const uint16_t *xt;       // else, batch >= kXtBatch: x transposed, [cols][xt_pad(batch)] fp16 (or null)
     int sparse_naive;         // 1 (ablation): one lane per row walks its own nonzeros, no balancing
 };
 
@@ -45,10 +46,14 @@ struct GroupArgs {
     KernelArgs item[kMaxGroup];
 };
 
+// Matrix-core form of the dense part (batch >= 2): batch columns in quads of 4.
+constexpr int mf_quads(int batch) { return (batch + 3) / 4; }
+
 // One launch configuration, chosen on the host.
 struct LaunchShape {
     int waves;                // waves per workgroup
     size_t dyn_lds;           // dynamic LDS bytes (staged x)
+    int mf;                   // 1: dense part on the matrix cores (batch >= 2)
 };
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
@@ -83,6 +88,29 @@ hipError_t launch_unpack(const void *packed, const uint16_t *lut, int rows, int 
 // Dynamic LDS of a workgroup that stages x for the outlier gathers: every
 // column of every batch column.
 inline size_t staged_x_bytes(int64_t cols, int batch) { return (size_t)cols * batch * 2; }
+
+// x transposed for the outlier gathers from batch kXtBatch on, when the
+// products reading one x carry at least kXtMinNnz nonzeros: all batch
+// columns of a column in one 16-byte word (padded with zeros).  Below that
+// the two extra launches (write, clear) cost more than the gathers save.
+constexpr int kXtBatch = 5;
+constexpr int64_t kXtMinNnz = 400000;
+constexpr int xt_pad(int batch) { return batch <= 2 ? 2 : (batch <= 4 ? 4 : 8); }
+inline size_t xt_bytes(int64_t cols, int batch)
+{
+    return batch < kXtBatch ? 0 : ((size_t)cols * xt_pad(batch) * 2 + 255) / 256 * 256;
+}
+// Transposed copies of up to kMaxGroup activations: written before the
+// product launch and cleared after it (the workspace is zero between calls).
+struct XtJobs {
+    int n;
+    int max_cols;
+    const uint16_t *x[kMaxGroup];
+    uint16_t *xt[kMaxGroup];
+    int cols[kMaxGroup];
+};
+hipError_t launch_xt_write(const XtJobs &j, int batch, hipStream_t stream);
+hipError_t launch_xt_clear(const XtJobs &j, int batch, hipStream_t stream);
 
 // Static LDS of a kernel: the pair table (dense modes) or the wave
 // reduction area (outlier-only mode).

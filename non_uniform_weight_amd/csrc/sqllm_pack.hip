@@ -204,7 +204,35 @@ __global__ void __launch_bounds__(256) unpack_kernel(const u32x4 *__restrict__ p
     }
 }
 
+// Job blockIdx.y: xt[c][b] = x[b][c] for b < batch, 0 up to the padded
+// width (CLEAR: xt = 0); one column per thread.
+template <bool CLEAR>
+__global__ void __launch_bounds__(256) xt_kernel(XtJobs j, int batch, int pad)
+{
+    const int k = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (k >= j.n || c >= j.cols[k]) return;
+    uint16_t *dst = j.xt[k] + (int64_t)c * pad;
+    for (int b = 0; b < pad; ++b) dst[b] = !CLEAR && b < batch ? j.x[k][(int64_t)b * j.cols[k] + c] : (uint16_t)0;
+}
+
 } // namespace
+
+hipError_t launch_xt_write(const XtJobs &j, int batch, hipStream_t stream)
+{
+    if (j.n < 1) return hipSuccess;
+    hipLaunchKernelGGL(xt_kernel<false>, dim3((unsigned)((j.max_cols + 255) / 256), (unsigned)j.n), dim3(256), 0,
+                       stream, j, batch, xt_pad(batch));
+    return hipGetLastError();
+}
+
+hipError_t launch_xt_clear(const XtJobs &j, int batch, hipStream_t stream)
+{
+    if (j.n < 1) return hipSuccess;
+    hipLaunchKernelGGL(xt_kernel<true>, dim3((unsigned)((j.max_cols + 255) / 256), (unsigned)j.n), dim3(256), 0,
+                       stream, j, batch, xt_pad(batch));
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void *packed, int *bad, hipStream_t stream)
 {

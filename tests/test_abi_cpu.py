@@ -49,6 +49,12 @@ def test_size_queries(nwpkg):
     assert nwpkg.packed_bytes(0, 256, 3) == 0
     assert nwpkg.workspace_bytes(22016, 8192, 1) >= 344 * 4
     assert nwpkg.workspace_bytes(22016, 8192, 9) == 0
+    # (sum, count) words per output, then at batch >= 5 x transposed to [cols][8]
+    assert nwpkg.workspace_bytes(100, 256, 1) == 2 * 64 * 8
+    assert nwpkg.workspace_bytes(100, 256, 2) == 2 * 2 * 64 * 8
+    assert nwpkg.workspace_bytes(100, 256, 4) == 2 * 4 * 64 * 8
+    assert nwpkg.workspace_bytes(100, 256, 8) == 2 * 8 * 64 * 8 + 256 * 8 * 2
+    assert nwpkg.workspace_bytes(64, 8192, 5) == 5 * 64 * 8 + 8192 * 8 * 2
 
 
 P = ctypes.c_void_p
@@ -163,10 +169,11 @@ def test_group_workspace_bytes(lib, nwpkg):
 
 
 def test_tuning_hook_bounds(lib):
-    assert lib.sqllm_test_tuning(0, 0, 65, 0, 0) == 3      # split above 64
-    assert lib.sqllm_test_tuning(0, 0, 0, 17, 0) == 3      # more than 16 waves
-    assert lib.sqllm_test_tuning(0, 0, 0, 0, 2) == 3       # outlier form 0 or 1
-    assert lib.sqllm_test_tuning(0, 0, 0, 0, 0) == 0
+    assert lib.sqllm_test_tuning(0, 0, 65, 0, 0, 0) == 3      # split above 64
+    assert lib.sqllm_test_tuning(0, 0, 0, 17, 0, 0) == 3      # more than 16 waves
+    assert lib.sqllm_test_tuning(0, 0, 0, 0, 2, 0) == 3       # outlier form 0 or 1
+    assert lib.sqllm_test_tuning(0, 0, 0, 0, 0, 2) == 3       # dense form 0 or 1
+    assert lib.sqllm_test_tuning(0, 0, 0, 0, 0, 0) == 0
 
 
 def test_quantize_argument_errors(lib):

@@ -313,6 +313,33 @@ def test_launch_configurations(bits, split, waves):
     assert_close(ys, y_ref, scale, TOL, "stream-ordered")
 
 
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("batch", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("form", ["matrix", "dot"])
+def test_dense_forms_every_batch(bits, batch, form):
+    """Both forms of the dense part -- the matrix-core form (default at batch
+    >= 2) and the v_dot2c form -- at every batch, fused and dense-only, with
+    16 waves (x staged in LDS for the outliers, beside the pair table and the
+    waves' x slots), 8 and 3 waves (outliers read x from global memory)."""
+    rng = np.random.default_rng(stable_seed(bits, batch, form, "forms"))
+    rows, cols = 193, 4096
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "5pct")
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    yd_ref, dscale = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    for waves in (16, 8, 3):
+        step(f"dense form={form} bits={bits} batch={batch} waves={waves}")
+        try:
+            nw().set_tuning(waves=waves, dot_only=1 if form == "dot" else 0)
+            y = d.fused()
+            yg = d.gemv()
+            torch.cuda.synchronize()
+        finally:
+            nw().set_tuning()
+        assert_close(y, y_ref, scale, TOL, f"fused waves={waves}")
+        assert_close(yg, yd_ref, dscale, TOL, f"gemv waves={waves}")
+
+
 # ------------------------------------------------------------ the evaluation workloads
 
 def _check_matrix(m: synth.Matrix, sel=None, ws=None):
@@ -445,6 +472,85 @@ def test_group_equals_single_calls(split):
         nw().set_tuning()
     for y, ys_, shape in zip(ys, singles, GROUP_CASES):
         assert np.array_equal(dev_to_u16(y), dev_to_u16(ys_)), f"group item {shape} differs from the single call"
+
+
+@pytest.mark.parametrize("batch", [4, 6, 8])
+def test_group_shared_x(batch):
+    """Products that share one x (as q, k and v do) share one transposed copy
+    of it for their outliers (at batch >= 5: their 600K+ nonzeros pass the
+    threshold); the product with another x (fewer nonzeros) reads x in place."""
+    rng = np.random.default_rng(stable_seed("group-shared-x", batch))
+    cols = 4096
+    x = (rng.standard_normal((batch, cols))).astype(np.float16).view(np.uint16)
+    x2 = (rng.standard_normal((batch, cols))).astype(np.float16).view(np.uint16)
+    shapes = [(300, "50pct", x), (129, "dense_row", x), (64, "full", x2), (193, "one", x)]
+    cases = []
+    for rows, sp, xx in shapes:
+        codes, lut, _, rp, col, val = _make_case(rng, rows, cols, 3, batch, sp)
+        cases.append((codes, lut, xx, rp, col, val))
+    xd, x2d = u16_to_dev(x), u16_to_dev(x2)
+    mats = [DevMatrix(c[0], c[1], 3, c[3], c[4], c[5], c[2]) for c in cases]
+    for d, (_, _, xx) in zip(mats, shapes):
+        d.x = xd if xx is x else x2d                 # one device copy per distinct x
+    ys = [torch.full((batch, d.rows), float("nan"), dtype=torch.float16, device="cuda") for d in mats]
+    step(f"group shared x batch {batch}")
+    nw().dense_sparse_gemv_group(_items(mats, ys), 3)
+    torch.cuda.synchronize()
+    for (codes, lut, xx, rp, col, val), y, (rows, sp, _) in zip(cases, ys, shapes):
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, xx)
+        assert_close(y, y_ref, scale, TOL, f"group item {rows} {sp}")
+
+
+def test_one_workspace_many_shapes():
+    """One workspace serves calls of different shapes and batches in any
+    order: after each call (transposed x included: the batch 8 and 6 calls
+    carry over 400K nonzeros) it is all zero again."""
+    rng = np.random.default_rng(stable_seed("ws-many"))
+    seq = [(300, 4096, 8, "50pct"), (1000, 2048, 1, "5pct"), (64, 8192, 6, "full"), (2000, 256, 2, "one"),
+           (129, 4096, 3, "dense_row")]
+    need = max(nw().workspace_bytes(r, c, b) for r, c, b, _ in seq)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rows, cols, batch, sp in seq + seq[::-1]:
+        codes, lut, x, rp, col, val = _make_case(rng, rows, cols, 3, batch, sp)
+        d = DevMatrix(codes, lut, 3, rp, col, val, x)
+        step(f"shared workspace {rows}x{cols} batch {batch} {sp}")
+        try:
+            nw().set_tuning(split=2, waves=8)
+            y = d.fused(ws=ws)
+            torch.cuda.synchronize()
+        finally:
+            nw().set_tuning()
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+        assert_close(y, y_ref, scale, TOL, f"{rows}x{cols} batch {batch}")
+        assert int(ws.count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("batch", [5, 8])
+def test_outliers_without_room_for_transposed_x(batch):
+    """A workspace that holds only the (sum, count) words: the outliers read
+    x in place; with the full workspace they read the transposed copy (526K
+    nonzeros, over the threshold)."""
+    rng = np.random.default_rng(stable_seed("no-xt", batch))
+    rows, cols = 257, 4096
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, 3, batch, "50pct")
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+    d = DevMatrix(codes, lut, 3, rp, col, val, x)
+    words = -(-rows // 64) * 64 * batch * 8
+    assert nw().workspace_bytes(rows, cols, batch) > words
+    small = torch.zeros(words, dtype=torch.uint8, device="cuda")
+    full = torch.zeros(nw().workspace_bytes(rows, cols, batch), dtype=torch.uint8, device="cuda")
+    step(f"outliers without transposed x, batch {batch}")
+    try:
+        nw().set_tuning(split=2, waves=8)           # split: the words are needed; 8 waves: x not in LDS
+        y_small = d.fused(ws=small)
+        y_full = d.fused(ws=full)
+        ys_small = d.spmv_add(d.gemv(ws=small), ws=small)
+        torch.cuda.synchronize()
+    finally:
+        nw().set_tuning()
+    assert_close(y_small, y_ref, scale, TOL, "fused, words only")
+    assert_close(y_full, y_ref, scale, TOL, "fused, full workspace")
+    assert_close(ys_small, y_ref, scale, TOL, "stream-ordered, words only")
 
 
 @pytest.mark.parametrize("density_bp", [0, 45])
