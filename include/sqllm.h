@@ -297,9 +297,9 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
  *   = 1 switches the outliers to the unbalanced form for the ablation of the
  *   balanced kernel (summary page, Appendix C, Table C.1): one thread per
  *   row walks the row's nonzeros; 0 restores the balanced form.  dot_only =
- *   1 keeps the dense part in the v_dot2c form at batch >= 2 (for the
- *   comparison with the matrix-core form those batches use by default); 0
- *   restores the default.  Shapes that no compiled kernel fits fail with
+ *   1 computes the dense part in the v_dot2c form instead of the default
+ *   matrix-core form (for the comparison of the two); 0 restores the
+ *   default.  Shapes that no compiled kernel fits fail with
  *   SQLLM_ERR_SHAPE.  Results agree within the stated tolerance for every
  *   shape; not thread-safe against concurrent calls. */
 sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive, int dot_only);

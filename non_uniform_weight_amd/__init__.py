@@ -326,7 +326,8 @@ def decode_weights(packed, lut, rows, cols, bits, stream=None) -> torch.Tensor:
 def set_tuning(target_wgs: int = 0, min_gps: int = 0, split: int = 0, waves: int = 0,
                sparse_naive: int = 0, dot_only: int = 0) -> None:
     """Test-only: launch shape of later calls (0 = default); sparse_naive=1 selects the unbalanced
-    one-thread-per-row outlier form, dot_only=1 the v_dot2c dense form at every batch (ablations)."""
+    one-thread-per-row outlier form, dot_only=1 the v_dot2c dense form instead of the matrix cores
+    (ablations)."""
     _check(_lib.sqllm_test_tuning(target_wgs, min_gps, split, waves, sparse_naive, dot_only),
            "sqllm_test_tuning")
 

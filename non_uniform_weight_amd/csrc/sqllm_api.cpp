@@ -22,7 +22,7 @@ struct Tuning {
     int force_split = 0;    // 0: choose; else workgroups per row tile
     int force_waves = 0;    // 0: choose; else waves per workgroup
     int sparse_naive = 0;   // ablation: 1 = outliers one lane per row, unbalanced
-    int dot_only = 0;       // ablation: 1 = dense part in the dot form at every batch
+    int dot_only = 0;       // ablation: 1 = dense part in the v_dot2c form instead of the matrix cores
     Tuning()
     {
         auto get = [](const char *name, int lo, int hi, int dflt) {
@@ -105,9 +105,10 @@ int choose_waves(int64_t workgroups)
     return workgroups > tuning().target_wgs ? kDefaultWaves : kMaxWaves;
 }
 
-// Dense part on the matrix cores from batch 2 on: the dot form's v_dot2c
-// count grows with the batch, one 4x4x4 matrix step covers 4 batch columns.
-int use_mf(int batch) { return batch >= 2 && !tuning().dot_only ? 1 : 0; }
+// Dense part on the matrix cores: one 4x4x4 step covers 4 columns of 4
+// batch columns where the dot form spends one v_dot2c per pair and batch
+// column (measured faster at every batch, 1 included).
+int use_mf(int batch) { (void)batch; return tuning().dot_only ? 0 : 1; }
 
 // Stage x in LDS for the outlier gathers when it fits beside the pair table
 // (in half of the LDS when two workgroups share a unit).

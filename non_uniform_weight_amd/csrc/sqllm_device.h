@@ -17,20 +17,29 @@
 //   v_perm_b32 straight from a packed byte (4-bit: every pair is a byte;
 //   3-bit: 12 of 16 pairs are the low six bits of a byte and the table repeats
 //   over the two ignored top bits, the other 4 pairs are gathered from the top
-//   bits).  The activation pairs are the same for every lane, so they stay in
-//   registers: lane n of each 16-lane row holds pairs 4n..4n+3 (and
-//   64+4n..64+4n+3) of the group, and v_dot2c_f32_f16 takes its x operand
-//   through a DPP row_newbcast:n, which hands lane n's pair to its whole row.
+//   bits).  The products run on the matrix cores (MF, the default): two
+//   lookups are a row's 4 consecutive weights, the B operand of one
+//   v_mfma_f32_4x4x4f16 step whose A (the same 4 activations of 4 batch
+//   columns for every row) is broadcast from the one block of lanes that
+//   holds it, so lane = row throughout and no activation passes through
+//   LDS.  The dot form (kept for comparison) instead keeps the activation
+//   pairs in registers -- lane n of each 16-lane row holds pairs 4n..4n+3
+//   (and 64+4n..64+4n+3) of the group -- and v_dot2c_f32_f16 takes its x
+//   operand through a DPP row_newbcast:n, which hands lane n's pair to its
+//   whole row.
 //
 //   outlier chunks: the tile's CSR nonzeros are cut into even shares, one per
 //   wave of the split (balanced whatever the per-row skew: §3.4 "Kernel
 //   Implementation", balanced sparse kernel; Appendix C), 64 per lane-wide
-//   chunk, a round of chunks in flight at a time, one chunk after each dense
-//   group.  Within a chunk the rows are non-decreasing: each row that starts
+//   chunk.  Within a chunk the rows are non-decreasing: each row that starts
 //   there marks its first lane, a ballot of the marks gives every lane its
-//   segment start, x is gathered (from LDS when it is staged there, else
-//   through the cache), and a DPP segmented scan sums each row's products;
-//   the row's own lane fetches its sum.
+//   segment start, x is gathered, and a DPP segmented scan sums each row's
+//   products; the row's own lane fetches its sum.  When all of x is staged
+//   in LDS a chunk follows each dense group; otherwise the chunks come after
+//   the dense groups, a round at a time (all of a round's gathers, then its
+//   scans), reading x through the cache or, from batch 5 on, from a
+//   transposed copy the call writes into the workspace (one load fetches
+//   every batch column of a column).
 //
 // The waves' fp32 row sums are added in a fixed order; the sparse part joins
 // the dense part in fp32 before the single rounding (kernel fusion).  A row
@@ -716,7 +725,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     constexpr bool DENSE = MODE != kSparseAdd;
     constexpr bool SPARSE = MODE != kDenseOnly;
     constexpr bool ADDY = MODE == kSparseAdd;
-    static_assert(!MF || (DENSE && B >= 2), "matrix-core form: dense modes, batch >= 2");
+    static_assert(!MF || DENSE, "matrix-core form: dense modes");
     constexpr int E = Format<BITS>::kEntries;
     constexpr int D = ring_depth(BITS, B, MF);
     constexpr int ITEMS = DENSE ? (64 * E) / 512 : 1; // table items per thread with 8 waves
@@ -1014,7 +1023,7 @@ hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream
 template <int BITS, int B, int MODE>
 hipError_t launch_group_form(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
-    if constexpr (MODE != kSparseAdd && B >= 2)
+    if constexpr (MODE != kSparseAdd)
         if (ls.mf) return launch_group_one<BITS, B, MODE, true>(g, ls, stream);
     return launch_group_one<BITS, B, MODE, false>(g, ls, stream);
 }
@@ -1022,7 +1031,7 @@ hipError_t launch_group_form(const GroupArgs &g, const LaunchShape &ls, hipStrea
 template <int BITS, int B, int MODE>
 hipError_t launch_form(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
-    if constexpr (MODE != kSparseAdd && B >= 2)
+    if constexpr (MODE != kSparseAdd)
         if (ls.mf) return launch_one<BITS, B, MODE, true>(a, ls, stream);
     return launch_one<BITS, B, MODE, false>(a, ls, stream);
 }

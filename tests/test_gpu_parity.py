@@ -314,11 +314,11 @@ def test_launch_configurations(bits, split, waves):
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-@pytest.mark.parametrize("batch", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("form", ["matrix", "dot"])
 def test_dense_forms_every_batch(bits, batch, form):
-    """Both forms of the dense part -- the matrix-core form (default at batch
-    >= 2) and the v_dot2c form -- at every batch, fused and dense-only, with
+    """Both forms of the dense part -- the matrix-core form (the default) and
+    the v_dot2c form -- at every batch, fused and dense-only, with
     16 waves (x staged in LDS for the outliers, beside the pair table and the
     waves' x slots), 8 and 3 waves (outliers read x from global memory)."""
     rng = np.random.default_rng(stable_seed(bits, batch, form, "forms"))
