@@ -312,7 +312,7 @@ def outlier_ablation(args) -> None:
 
 def batch_ablation(args) -> None:
     """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4 and 8,
-    batches 2..8 in both dense forms (matrix-core, the default, and v_dot2c):
+    in both dense forms (matrix-core, the default, and v_dot2c):
     µs per product and effective GB/s (bytes grow only by x and y, the math by
     the batch), graph-timed over copies of the inputs (>= 1.2 GB)."""
     import numpy as np
@@ -324,8 +324,8 @@ def batch_ablation(args) -> None:
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     out = []
-    for batch, form in [(1, "dot"), (2, "matrix"), (2, "dot"), (4, "matrix"), (4, "dot"), (8, "matrix"), (8, "dot")]:
-        nw.set_tuning(dot_only=1 if form == "dot" and batch > 1 else 0)
+    for batch, form in [(b, f) for b in (1, 2, 4, 8) for f in ("matrix", "dot")]:
+        nw.set_tuning(dot_only=1 if form == "dot" else 0)
         for i, spec in enumerate(synth.workload(4, batch=batch)):
             m = synth.make_matrix(spec, seed=args.seed, workload=4, index=i)
             packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
