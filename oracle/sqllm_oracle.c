@@ -38,6 +38,8 @@
  *   The 32b bytes of (r, g), pieces in order, form the group's byte string.
  *   Codes pair up: pair p holds codes 2p and 2p+1 as
  *   value = code[2p] | code[2p+1] << b.
+ *   2-bit: byte p of the string holds pair 2p in its low four bits and
+ *   pair 2p+1 in its high four bits.
  *   4-bit: byte p of the string is pair p.
  *   3-bit: the string is 8 units of 12 bytes, unit u holding codes
  *   32u .. 32u+31 as pairs p = 0..15 of that unit; pair p < 12 is the low
@@ -125,6 +127,7 @@ static int64_t string_byte_offset(int64_t row, int64_t group, int64_t k, int64_t
 static unsigned pair_value(const uint8_t *packed, int64_t row, int64_t group, int64_t p, int64_t cols, int bits)
 {
     if (bits == 4) return packed[string_byte_offset(row, group, p, cols, bits)];
+    if (bits == 2) return (packed[string_byte_offset(row, group, p / 2, cols, bits)] >> (4 * (p % 2))) & 0xFu;
     int64_t unit = p / 16, pu = p % 16, base = 12 * unit;
     if (pu < 12) return packed[string_byte_offset(row, group, base + pu, cols, bits)] & 0x3Fu;
     int64_t q = pu - 12;

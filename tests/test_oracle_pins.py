@@ -96,18 +96,22 @@ def test_packed_bytes_formula():
     assert oracle.packed_bytes(130, 512, 3) == 3 * 64 * 512 * 3 // 8
     assert oracle.packed_bytes(64, 256, 4) == 64 * 256 // 2
     assert oracle.packed_bytes(22016, 8192, 3) == 22016 * 8192 * 3 // 8
+    assert oracle.packed_bytes(65, 512, 2) == 2 * 64 * 512 // 4
 
 
 def group_string(codes_row_group: np.ndarray, bits: int) -> bytes:
     """The 32*bits-byte string of one (row, 256-column group), from the layout
     definition: pairs p = code[2p] | code[2p+1] << bits; 4-bit: byte p is
-    pair p; 3-bit: units of 12 bytes / 16 pairs, pair p < 12 in the low six
+    pair p; 2-bit: byte p holds pair 2p in its low and pair 2p+1 in its high
+    four bits; 3-bit: units of 12 bytes / 16 pairs, pair p < 12 in the low six
     bits of unit byte p, pair 12+q spread two bits at a time over the top two
     bits of unit bytes q, 4+q, 8+q."""
     c = [int(v) for v in codes_row_group]
     pairs = [c[2 * p] | (c[2 * p + 1] << bits) for p in range(128)]
     if bits == 4:
         return bytes(pairs)
+    if bits == 2:
+        return bytes(pairs[2 * p] | (pairs[2 * p + 1] << 4) for p in range(64))
     out = bytearray(96)
     for u in range(8):
         unit = pairs[16 * u:16 * u + 16]
@@ -134,7 +138,7 @@ def pack_from_definition(codes: np.ndarray, bits: int) -> np.ndarray:
     return buf
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols", [(1, 256), (63, 512), (65, 256), (130, 768)])
 def test_unpack_roundtrip_with_independent_packer(bits, rows, cols):
     rng = np.random.default_rng(rows * 1000 + cols + bits)
@@ -200,7 +204,7 @@ def _make_case(rng, rows, cols, bits, batch, sparsity):
     return codes, lut, x, rp, col, val
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols,batch", [(1, 256, 1), (2, 512, 3), (7, 768, 8), (65, 256, 2), (257, 512, 1)])
 @pytest.mark.parametrize("sparsity", SPARSITY)
 def test_product_matches_brute_force(bits, rows, cols, batch, sparsity):

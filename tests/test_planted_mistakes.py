@@ -48,6 +48,9 @@ MUTANTS = {
     "nibbles_swapped": (
         "codes[r * cols + c] = (uint8_t)((j % 2 ? v >> bits : v) & mask);",
         "codes[r * cols + c] = (uint8_t)((j % 2 ? v : v >> bits) & mask);"),
+    "two_bit_pair_nibbles_swapped": (
+        "return (packed[string_byte_offset(row, group, p / 2, cols, bits)] >> (4 * (p % 2))) & 0xFu;",
+        "return (packed[string_byte_offset(row, group, p / 2, cols, bits)] >> (4 * (1 - p % 2))) & 0xFu;"),
     "extra_pairs_unit_stride": (
         "int64_t unit = p / 16, pu = p % 16, base = 12 * unit;",
         "int64_t unit = p / 16, pu = p % 16, base = 16 * unit;"),
