@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--bits", type=int, default=3, choices=(3, 4))
+    p.add_argument("--bits", type=int, default=3, choices=(2, 3, 4))
     p.add_argument("--density-bp", type=int, default=45, help="outlier density in basis points (45 = 0.45%%)")
     p.add_argument("--layers", type=int, default=80)
     p.add_argument("--seed", type=int, default=0)

@@ -7,7 +7,8 @@
  *     outlier / sensitive weights in CSR form with fp16 values, 16-bit column
  *     indices and row pointers (nnz of row i = row_ptr[i+1] - row_ptr[i]).
  *   - §3.4 "Kernel Implementation": D is stored as a 2-D array of b-bit
- *     indices (b = 3 or 4); index code[r][c] selects one of 2^b fp16
+ *     indices (b = 3 or 4; b = 2 as in Appendix F, Tables F.8 and F.10);
+ *     index code[r][c] selects one of 2^b fp16
  *     centroids in the lookup table of output channel r; the dequantized
  *     weights multiply an fp16 activation vector.  A balanced sparse kernel
  *     computes S x, fused with the dense part into one output.
@@ -55,6 +56,8 @@
  *   Codes go in pairs: pair p (0..127) holds codes 2p and 2p+1 as the
  *   2b-bit value code[2p] | code[2p+1] << b.
  *     4-bit: byte p of the string is pair p.
+ *     2-bit: byte p of the string holds pair 2p in its low four bits and
+ *       pair 2p+1 in its high four bits.
  *     3-bit: the string is 8 units of 12 bytes; unit u holds pairs
  *       16u .. 16u+15.  Pair 16u+p for p < 12 is the low six bits of unit
  *       byte p.  Pair 16u+12+q (q = 0..3) stores its bits [2k, 2k+2) in the
@@ -101,7 +104,7 @@ extern "C" {
 typedef enum {
     SQLLM_OK = 0,
     SQLLM_ERR_NULL = 1,       /* a required pointer is NULL */
-    SQLLM_ERR_BITS = 2,       /* bits not 3 or 4 */
+    SQLLM_ERR_BITS = 2,       /* bits not 2, 3 or 4 */
     SQLLM_ERR_SHAPE = 3,      /* rows / cols / nnz out of range */
     SQLLM_ERR_BATCH = 4,      /* batch not in [1, 8] */
     SQLLM_ERR_ALIGN = 5,      /* a pointer is not aligned as required */

@@ -230,7 +230,7 @@ const char *sqllm_status_string(sqllm_status s)
     switch (s) {
     case SQLLM_OK: return "SQLLM_OK";
     case SQLLM_ERR_NULL: return "SQLLM_ERR_NULL: required pointer is NULL";
-    case SQLLM_ERR_BITS: return "SQLLM_ERR_BITS: bits must be 3 or 4";
+    case SQLLM_ERR_BITS: return "SQLLM_ERR_BITS: bits must be 2, 3 or 4";
     case SQLLM_ERR_SHAPE: return "SQLLM_ERR_SHAPE: rows/cols/nnz out of range";
     case SQLLM_ERR_BATCH: return "SQLLM_ERR_BATCH: batch must be in [1, 8]";
     case SQLLM_ERR_ALIGN: return "SQLLM_ERR_ALIGN: pointer not aligned as required";
@@ -244,7 +244,7 @@ const char *sqllm_status_string(sqllm_status s)
 
 size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits)
 {
-    if ((bits != 3 && bits != 4) || check_shape(rows, cols) != SQLLM_OK) return 0;
+    if ((bits < 2 || bits > 4) || check_shape(rows, cols) != SQLLM_OK) return 0;
     return (size_t)(tiles_of(rows) * kTileRows * cols * bits / 8);
 }
 
@@ -257,7 +257,7 @@ size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch)
 sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed, hipStream_t stream)
 {
     if (!codes || !packed) return SQLLM_ERR_NULL;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     sqllm_status st = check_shape(rows, cols);
     if (st != SQLLM_OK) return st;
     if (!aligned(codes, 16) || !aligned(packed, 16)) return SQLLM_ERR_ALIGN;
@@ -289,7 +289,7 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     if (!packed || !lut) return SQLLM_ERR_NULL;
     sqllm_status st = common_checks(rows, cols, x, batch, y);
     if (st != SQLLM_OK) return st;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     st = sparse_checks(row_ptr, col_idx, val, nnz, cols);
     if (st != SQLLM_OK) return st;
     if (!aligned(packed, 16) || !aligned(lut, 16)) return SQLLM_ERR_ALIGN;
@@ -356,7 +356,7 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
 {
     if (!items) return SQLLM_ERR_NULL;
     if (n < 1 || n > kMaxGroup) return SQLLM_ERR_SHAPE;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     if (batch < 1 || batch > kMaxBatch) return SQLLM_ERR_BATCH;
     // every product's arguments first, as for the single call
     for (int i = 0; i < n; ++i) {
@@ -542,7 +542,7 @@ sqllm_status sqllm_kmeans_lut(const uint16_t *dense, const float *sens, int64_t 
     sqllm_status st = quantize_shape(dense, rows, cols);
     if (st != SQLLM_OK) return st;
     if (!codes || !lut) return SQLLM_ERR_NULL;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     if (iters < 0 || iters > 1000) return SQLLM_ERR_SHAPE;
     if (!aligned(lut, 2) || (sens && !aligned(sens, 4))) return SQLLM_ERR_ALIGN;
     if (launch_kmeans(dense, sens, (int)rows, (int)cols, bits, iters, codes, lut, stream) != hipSuccess)
@@ -570,7 +570,7 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
                                hipStream_t stream)
 {
     if (!packed || !codes) return SQLLM_ERR_NULL;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     sqllm_status st = check_shape(rows, cols);
     if (st != SQLLM_OK) return st;
     if (!aligned(packed, 16) || !aligned(codes, 16)) return SQLLM_ERR_ALIGN;
@@ -583,7 +583,7 @@ sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t 
                                uint16_t *w, hipStream_t stream)
 {
     if (!packed || !lut || !w) return SQLLM_ERR_NULL;
-    if (bits != 3 && bits != 4) return SQLLM_ERR_BITS;
+    if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     sqllm_status st = check_shape(rows, cols);
     if (st != SQLLM_OK) return st;
     if (!aligned(packed, 16) || !aligned(w, 16) || !aligned(lut, 2)) return SQLLM_ERR_ALIGN;

@@ -111,6 +111,16 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
 {
     if constexpr (BITS == 4) {
         return __builtin_amdgcn_perm(d[P >> 2], lane4, addr_sel<P & 3>());
+    } else if constexpr (BITS == 2) {
+        // pair P is nibble P % 2 of string byte P / 2; an odd pair's byte is
+        // taken from the dword shifted down by four bits (one shift per
+        // dword, shared by its four odd pairs).  The table repeats over the
+        // byte's other nibble.
+        constexpr int k = (P >> 1) & 3;
+        if constexpr ((P & 1) == 0)
+            return __builtin_amdgcn_perm(d[P >> 3], lane4, addr_sel<k>());
+        else
+            return __builtin_amdgcn_perm(d[P >> 3] >> 4, lane4, addr_sel<k>());
     } else {
         constexpr int u = P / 16, pu = P % 16;
         if constexpr (pu < 12) {
@@ -146,7 +156,7 @@ struct GroupRegs {
 constexpr int ring_depth(int bits, int batch, bool mf)
 {
     const int per = 8 * bits + (mf ? 8 * mf_quads(batch) : 8 * batch);
-    const int d = ((bits == 3 ? 80 : 72) - (mf ? 16 * mf_quads(batch) : 0)) / per;
+    const int d = ((bits <= 3 ? 80 : 72) - (mf ? 16 * mf_quads(batch) : 0)) / per;
     return d < 1 ? 1 : (d > 3 ? 3 : d);
 }
 
@@ -470,14 +480,20 @@ __device__ __forceinline__ void table_items_load(TableItems<BITS, N> &it, const 
 {
     constexpr int E = Format<BITS>::kEntries;
     const int r = min(row0 + (idx0 & 63), rows - 1);
-    const u32x4 *lrow = (const u32x4 *)(lut + (int64_t)r * E);
+    if constexpr (E == 4) { // 8-byte table rows
+        const u32x2 v = *(const u32x2 *)(lut + (int64_t)r * E);
+        it.lw[0] = v.x;
+        it.lw[1] = v.y;
+    } else {
+        const u32x4 *lrow = (const u32x4 *)(lut + (int64_t)r * E);
 #pragma unroll
-    for (int q = 0; q < E / 8; ++q) {
-        const u32x4 v = lrow[q];
-        it.lw[4 * q + 0] = v.x;
-        it.lw[4 * q + 1] = v.y;
-        it.lw[4 * q + 2] = v.z;
-        it.lw[4 * q + 3] = v.w;
+        for (int q = 0; q < E / 8; ++q) {
+            const u32x4 v = lrow[q];
+            it.lw[4 * q + 0] = v.x;
+            it.lw[4 * q + 1] = v.y;
+            it.lw[4 * q + 2] = v.z;
+            it.lw[4 * q + 3] = v.w;
+        }
     }
 #pragma unroll
     for (int k = 0; k < N; ++k) { // items past the table load a valid entry and are not stored
@@ -501,6 +517,9 @@ __device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it,
             const uint32_t v = it.lo[k] | hi;
             if constexpr (BITS == 4) {
                 tab[(h | (c << 4)) * 64 + l] = v;
+            } else if constexpr (BITS == 2) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) tab[(h | (c << 2) | (j << 4)) * 64 + l] = v;
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) tab[(h | (c << 3) | (j << 6)) * 64 + l] = v;
@@ -728,7 +747,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     static_assert(!MF || DENSE, "matrix-core form: dense modes");
     constexpr int E = Format<BITS>::kEntries;
     constexpr int D = ring_depth(BITS, B, MF);
-    constexpr int ITEMS = DENSE ? (64 * E) / 512 : 1; // table items per thread with 8 waves
+    constexpr int ITEMS = DENSE && E >= 8 ? (64 * E) / 512 : 1; // table items per thread with 8 waves
     __shared__ __align__(16) uint32_t tab[DENSE ? kTableBytes / 4 : kMaxWaves * B * 64];
     extern __shared__ __align__(16) uint32_t dyn[];
 

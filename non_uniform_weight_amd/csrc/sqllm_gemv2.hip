@@ -1,0 +1,16 @@
+// sqllm_gemv2.hip -- instantiations of the 2-bit gemv kernels (y = D x).
+#include "sqllm_device.h"
+
+namespace sqllm {
+
+hipError_t launch_gemv2(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_batch<2, kDenseOnly>(a, batch, ls, stream);
+}
+
+hipError_t launch_group_gemv2(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
+{
+    return dev::launch_group_batch<2, kDenseOnly>(g, batch, ls, stream);
+}
+
+} // namespace sqllm

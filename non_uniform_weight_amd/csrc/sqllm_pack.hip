@@ -15,6 +15,10 @@
 
 namespace sqllm {
 
+hipError_t launch_fused2(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_gemv2(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_fused2(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_gemv2(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_fused3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_fused4(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_gemv3(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
@@ -29,8 +33,12 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
                                hipStream_t stream)
 {
     switch (mode) {
-    case kFused: return bits == 3 ? launch_fused3(a, batch, ls, stream) : launch_fused4(a, batch, ls, stream);
-    case kDenseOnly: return bits == 3 ? launch_gemv3(a, batch, ls, stream) : launch_gemv4(a, batch, ls, stream);
+    case kFused:
+        return bits == 2 ? launch_fused2(a, batch, ls, stream)
+                         : bits == 3 ? launch_fused3(a, batch, ls, stream) : launch_fused4(a, batch, ls, stream);
+    case kDenseOnly:
+        return bits == 2 ? launch_gemv2(a, batch, ls, stream)
+                         : bits == 3 ? launch_gemv3(a, batch, ls, stream) : launch_gemv4(a, batch, ls, stream);
     case kSparseAdd: return launch_spmv_add(a, batch, ls, stream);
     }
     return hipErrorInvalidValue;
@@ -41,9 +49,13 @@ hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mo
 {
     switch (mode) {
     case kFused:
-        return bits == 3 ? launch_group_fused3(g, batch, ls, stream) : launch_group_fused4(g, batch, ls, stream);
+        return bits == 2   ? launch_group_fused2(g, batch, ls, stream)
+               : bits == 3 ? launch_group_fused3(g, batch, ls, stream)
+                           : launch_group_fused4(g, batch, ls, stream);
     case kDenseOnly:
-        return bits == 3 ? launch_group_gemv3(g, batch, ls, stream) : launch_group_gemv4(g, batch, ls, stream);
+        return bits == 2   ? launch_group_gemv2(g, batch, ls, stream)
+               : bits == 3 ? launch_group_gemv3(g, batch, ls, stream)
+                           : launch_group_gemv4(g, batch, ls, stream);
     case kSparseAdd: break;
     }
     return hipErrorInvalidValue;
@@ -75,6 +87,9 @@ __device__ __forceinline__ void pairs_to_string(const uint32_t *pair, uint32_t *
     if constexpr (BITS == 4) {
 #pragma unroll
         for (int p = 0; p < 128; ++p) put_byte<4>(w, p, pair[p]);
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int p = 0; p < 64; ++p) put_byte<2>(w, p, pair[2 * p] | (pair[2 * p + 1] << 4));
     } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -94,6 +109,8 @@ __device__ __forceinline__ uint32_t string_pair(const uint32_t *w, int p)
 {
     if constexpr (BITS == 4) {
         return get_byte<4>(w, p);
+    } else if constexpr (BITS == 2) {
+        return (get_byte<2>(w, p >> 1) >> (4 * (p & 1))) & 0xFu;
     } else {
         const int u = p >> 4, pu = p & 15;
         if (pu < 12) return get_byte<3>(w, 12 * u + pu) & 0x3Fu;
@@ -239,7 +256,9 @@ hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void 
     const int groups = cols / 256, tiles = (rows + 63) / 64;
     const int64_t total = (int64_t)tiles * groups * 64;
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    if (bits == 3)
+    if (bits == 2)
+        hipLaunchKernelGGL(pack_kernel<2>, grid, block, 0, stream, codes, rows, cols, groups, total, (u32x4 *)packed, bad);
+    else if (bits == 3)
         hipLaunchKernelGGL(pack_kernel<3>, grid, block, 0, stream, codes, rows, cols, groups, total, (u32x4 *)packed, bad);
     else
         hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, stream, codes, rows, cols, groups, total, (u32x4 *)packed, bad);
@@ -254,12 +273,16 @@ hipError_t launch_unpack(const void *packed, const uint16_t *lut, int rows, int 
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
     const u32x4 *p = (const u32x4 *)packed;
     if (w) {
-        if (bits == 3)
+        if (bits == 2)
+            hipLaunchKernelGGL((unpack_kernel<2, true>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);
+        else if (bits == 3)
             hipLaunchKernelGGL((unpack_kernel<3, true>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);
         else
             hipLaunchKernelGGL((unpack_kernel<4, true>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);
     } else {
-        if (bits == 3)
+        if (bits == 2)
+            hipLaunchKernelGGL((unpack_kernel<2, false>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);
+        else if (bits == 3)
             hipLaunchKernelGGL((unpack_kernel<3, false>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);
         else
             hipLaunchKernelGGL((unpack_kernel<4, false>), grid, block, 0, stream, p, lut, rows, cols, groups, total, codes, w);

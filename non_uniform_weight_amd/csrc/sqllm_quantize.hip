@@ -372,7 +372,10 @@ hipError_t launch_outlier_extract(const uint16_t *w, const float *sens, int rows
 hipError_t launch_kmeans(const uint16_t *dense, const float *sens, int rows, int cols, int bits, int iters,
                          uint8_t *codes, uint16_t *lut, hipStream_t stream)
 {
-    if (bits == 3)
+    if (bits == 2)
+        hipLaunchKernelGGL(kmeans_kernel<4>, dim3((unsigned)rows), dim3(kKmThreads), 0, stream, dense, sens, cols,
+                           iters, codes, lut);
+    else if (bits == 3)
         hipLaunchKernelGGL(kmeans_kernel<8>, dim3((unsigned)rows), dim3(kKmThreads), 0, stream, dense, sens, cols,
                            iters, codes, lut);
     else

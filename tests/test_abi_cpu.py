@@ -47,6 +47,8 @@ def test_size_queries(nwpkg):
     assert nwpkg.packed_bytes(64, 100, 3) == 0
     assert nwpkg.packed_bytes(64, 256, 5) == 0
     assert nwpkg.packed_bytes(0, 256, 3) == 0
+    assert nwpkg.packed_bytes(65, 512, 2) == 2 * 64 * 512 // 4
+    assert nwpkg.packed_bytes(64, 256, 1) == 0
     assert nwpkg.workspace_bytes(22016, 8192, 1) >= 344 * 4
     assert nwpkg.workspace_bytes(22016, 8192, 9) == 0
     # (sum, count) words per output, then at batch >= 5 x transposed to [cols][8]
@@ -81,7 +83,7 @@ def test_gemv_argument_errors(lib):
     assert gemv(lib, lut=None) == 1
     assert gemv(lib, x=None) == 1
     assert gemv(lib, y=None) == 1
-    assert gemv(lib, bits=2) == 2
+    assert gemv(lib, bits=1) == 2
     assert gemv(lib, bits=5) == 2
     assert gemv(lib, rows=0) == 3
     assert gemv(lib, cols=0) == 3
@@ -124,7 +126,7 @@ def test_pack_and_reader_argument_errors(lib):
     assert lib.sqllm_pack(P(0x100001), 64, 256, 3, B16, None) == 5
     assert lib.sqllm_test_unpack(A16, 64, 256, 3, None, None) == 1
     assert lib.sqllm_test_decode(A16, None, 64, 256, 3, B16, None) == 1
-    assert lib.sqllm_test_decode(A16, B16, 64, 256, 2, B16, None) == 2
+    assert lib.sqllm_test_decode(A16, B16, 64, 256, 1, B16, None) == 2
 
 
 def _products(nwpkg, n, **over):
@@ -145,7 +147,7 @@ def test_group_argument_errors(lib, nwpkg):
     assert lib.sqllm_dense_sparse_gemv_group(None, 2, 3, 1, A16, 1 << 20, None) == 1
     assert group(lib, nwpkg, n=0) == 3
     assert group(lib, nwpkg, n=9) == 3
-    assert group(lib, nwpkg, bits=2) == 2
+    assert group(lib, nwpkg, bits=1) == 2
     assert group(lib, nwpkg, batch=9) == 4
     assert group(lib, nwpkg, packed=None) == 1
     assert group(lib, nwpkg, x=None) == 1
@@ -220,7 +222,7 @@ def test_quantize_argument_errors(lib):
         return lib.sqllm_kmeans_lut(d, sens, 64, 256, bits, iters, codes, lut, None)
     assert km(d=None) == 1
     assert km(codes=None) == 1
-    assert km(bits=2) == 2
+    assert km(bits=1) == 2
     assert km(iters=1001) == 3
     assert km(lut=P(0x100001)) == 5
     assert km(sens=P(0x100002)) == 5
@@ -253,3 +255,16 @@ def test_bytes_accounting_against_table1(nwpkg):
     nnz = [int(round(0.0045 * r * c)) for r, c in LLAMA7B]
     stored = sum(nwpkg.algorithmic_bytes(r, c, 3, n, 1) - 2 * c - 2 * r for (r, c), n in zip(LLAMA7B, nnz))
     assert 3.17 < 8 * stored / weights < 3.19
+
+
+LLAMA2_13B = [(5120, 5120)] * 4 + [(13824, 5120)] * 2 + [(5120, 13824)]
+
+
+def test_bytes_accounting_2bit_against_appendix_f(nwpkg):
+    """Dense-only 2-bit SqueezeLLM on LLaMA2-13B's linear layers: the pages
+    print 2.01 average bits (summary page, Appendix F, Table F.8) -- 2 bits of
+    code plus four fp16 centroids per row."""
+    weights = sum(r * c for r, c in LLAMA2_13B)
+    stored = sum(nwpkg.algorithmic_bytes(r, c, 2, 0, 1) - 2 * c - 2 * r for r, c in LLAMA2_13B)
+    avg = 8 * stored / weights
+    assert int(avg * 100) / 100 == 2.01

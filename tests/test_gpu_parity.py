@@ -27,7 +27,7 @@ def _f16(a):
 
 # ------------------------------------------------------------ pack / unpack
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols", [(1, 256), (63, 512), (65, 256), (130, 768), (257, 1024)])
 def test_pack_bytes_equal_definition(bits, rows, cols):
     step(f"pack bits={bits} rows={rows} cols={cols}")
@@ -42,7 +42,7 @@ def test_pack_bytes_equal_definition(bits, rows, cols):
     assert np.array_equal(oracle.unpack(packed.cpu().numpy(), rows, cols, bits), codes)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols", [(1, 256), (65, 768), (300, 2048)])
 def test_unpack_and_decode_bit_exact(bits, rows, cols):
     step(f"unpack/decode bits={bits} rows={rows} cols={cols}")
@@ -81,7 +81,7 @@ SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8)
 SPARSITY = ["none", "one", "5pct", "50pct", "full", "empty_rows", "dense_row"]
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols,batch", SHAPES)
 @pytest.mark.parametrize("sparsity", SPARSITY)
 def test_fused_matches_oracle(bits, rows, cols, batch, sparsity):
@@ -95,7 +95,7 @@ def test_fused_matches_oracle(bits, rows, cols, batch, sparsity):
     assert_close(y, y_ref, scale, TOL, "fused")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rows,cols,batch", SHAPES)
 def test_gemv_matches_oracle(bits, rows, cols, batch):
     step(f"gemv bits={bits} rows={rows} cols={cols} batch={batch}")
@@ -135,7 +135,7 @@ def test_spmv_add_without_outliers_is_noop():
     assert np.array_equal(dev_to_u16(y), y0)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_stream_ordered_pair_equals_fused(bits):
     step(f"gemv+spmv_add vs fused bits={bits}")
     rng = np.random.default_rng(31 + bits)
@@ -290,7 +290,7 @@ def test_workspace_shared_across_shapes():
     assert int(ws.view(torch.int32).abs().sum().item()) == 0
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("split,waves", [(1, 1), (1, 16), (2, 8), (3, 5), (7, 2), (16, 1), (0, 0)])
 def test_launch_configurations(bits, split, waves):
     """Column splits and waves per workgroup of every kind give the same
@@ -313,7 +313,7 @@ def test_launch_configurations(bits, split, waves):
     assert_close(ys, y_ref, scale, TOL, "stream-ordered")
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("form", ["matrix", "dot"])
 def test_dense_forms_every_batch(bits, batch, form):
@@ -437,7 +437,7 @@ GROUP_CASES = [(193, 4096, "5pct"), (64, 256, "none"), (1000, 2048, "empty_rows"
                (300, 8192, "one"), (129, 512, "dense_row")]
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_group_matches_oracle(bits, batch):
     """Products of different shapes, with and without outliers (two launches),

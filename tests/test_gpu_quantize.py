@@ -198,7 +198,7 @@ def kmeans_on_gpu(d, bits, iters, sens=None):
 
 
 KM_CASES = [(1, 7, 3, 20), (37, 300, 3, 20), (37, 300, 4, 0), (37, 300, 4, 1), (130, 1000, 4, 20),
-            (65, 4096, 3, 30)]
+            (65, 4096, 3, 30), (37, 300, 2, 20), (130, 1000, 2, 1)]
 
 
 @pytest.mark.parametrize("weighted", [False, True])
@@ -312,3 +312,30 @@ def test_weighted_pipeline_with_sensitive_values():
     assert np.array_equal(codes.cpu().numpy(), o_codes)
     y_ref, scale = oracle.dense_sparse_gemv(o_codes, o_lut, bits, o_rp, o_col, o_val, x)
     assert_close(y, y_ref, scale, what="weighted pipeline")
+
+
+def test_two_bit_pipeline_with_a_tenth_percent_sparse():
+    """The pages' 2-bit setting (Appendix F, Tables F.8 / F.10): 0.05%
+    outliers (0.025% per tail) plus 0.05% sensitive values to S, four
+    weighted centroids per row, packed and multiplied, against the oracle's
+    own pipeline."""
+    rows, cols, bits = 300, 2048, 2
+    w = heavy("twobit", rows, cols)
+    sens = fisher_like("twobit-fisher", rows, cols)
+    x = np.random.default_rng(stable_seed("twobit-x")).normal(0, 1, (2, cols)).astype(np.float16).view(np.uint16)
+    step("2-bit pipeline")
+    wd, sd = u16_to_dev(w), torch.from_numpy(sens).cuda()
+    t_min, t_max, t_s, nnz = nw().outlier_thresholds(wd, 250, sd, 500)
+    rp, col, val, dense, sdense = nw().outlier_extract(wd, t_min, t_max, nnz, sd, t_s)
+    codes, lut = nw().kmeans_lut(dense, bits, 25, sdense)
+    packed = nw().pack(codes, bits)
+    y = nw().dense_sparse_gemv(packed, lut, bits, rp, col, val, u16_to_dev(x))
+    torch.cuda.synchronize()
+    o_min, o_max, o_s, o_nnz = q.split_thresholds(w, 250, sens, 500)
+    assert nnz == o_nnz and 0.0009 < nnz / (rows * cols) < 0.0011
+    o_rp, o_col, o_val, o_dense = q.extract(w, o_min, o_max, sens, o_s)
+    o_codes, o_lut = q.kmeans_lut(o_dense, q.dense_sensitivity(sens, o_rp, o_col), bits, 25)
+    assert np.array_equal(dev_to_u16(lut), o_lut)
+    assert np.array_equal(codes.cpu().numpy(), o_codes)
+    y_ref, scale = oracle.dense_sparse_gemv(o_codes, o_lut, bits, o_rp, o_col, o_val, x)
+    assert_close(y, y_ref, scale, 5e-3, what="2-bit pipeline")
