@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--ablation", choices=("outliers", "batch", "offline"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
-                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8 in both dense forms; offline: the "
+                        "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8, 16 in both dense forms; offline: the "
                         "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
@@ -311,8 +311,9 @@ def outlier_ablation(args) -> None:
 
 
 def batch_ablation(args) -> None:
-    """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4 and 8,
-    in both dense forms (matrix-core, the default, and v_dot2c):
+    """The three 65B shapes (3-bit, 0.45% outliers) at batch 1, 2, 4, 8 and
+    16, in both dense forms (matrix-core, the default, and v_dot2c, which is
+    built up to batch 8):
     µs per product and effective GB/s (bytes grow only by x and y, the math by
     the batch), graph-timed over copies of the inputs (>= 1.2 GB)."""
     import numpy as np
@@ -324,7 +325,7 @@ def batch_ablation(args) -> None:
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     out = []
-    for batch, form in [(b, f) for b in (1, 2, 4, 8) for f in ("matrix", "dot")]:
+    for batch, form in [(b, f) for b in (1, 2, 4, 8, 16) for f in ("matrix", "dot") if b <= 8 or f == "matrix"]:
         nw.set_tuning(dot_only=1 if form == "dot" else 0)
         for i, spec in enumerate(synth.workload(4, batch=batch)):
             m = synth.make_matrix(spec, seed=args.seed, workload=4, index=i)

@@ -14,7 +14,7 @@
  *     computes S x, fused with the dense part into one output.
  *   - §3.4 "The 3/4-bit storage format": every index takes exactly b bits.
  *   - §3.4 "The Memory-Bound Analysis": batch-1 generation is a
- *     matrix-vector product; batches up to 8 are accepted here.
+ *     matrix-vector product; batches up to 16 are accepted here.
  *
  *   y[b][r] = sum_c LUT[r][code[r][c]] * x[b][c]
  *           + sum_{i=row_ptr[r]}^{row_ptr[r+1]-1} val[i] * x[b][col_idx[i]]
@@ -42,7 +42,7 @@
  *     non-decreasing, col_idx[i] < cols, x and y do not overlap, inputs finite.
  *     Duplicate (row, column) outlier entries are summed.
  *   - rows >= 1; cols >= 256 and a multiple of 256; cols <= 65536 when
- *     outliers are given (16-bit column indices); nnz < 2^31; 1 <= batch <= 8.
+ *     outliers are given (16-bit column indices); nnz < 2^31; 1 <= batch <= 16.
  *
  * Packed code layout (the pages fix only that every index takes exactly b bits; the
  * arrangement below is this library's, chosen so that each 64-lane wave
@@ -79,7 +79,7 @@
  * any sequence of calls, of any shapes it is large enough for, that are
  * ordered on one stream.  Calls that may run concurrently need separate
  * workspaces.  At batch >= 5 the workspace also holds, behind the words, a
- * transposed copy of x ([cols][8] fp16) from which the outliers
+ * transposed copy of x ([cols][8] fp16, [cols][16] above batch 8) from which the outliers
  * read all batch columns of a column in one load; the call writes it before
  * its product kernel and clears it after, so the whole workspace is zero
  * again when the call's work on the stream is done.  When a call does not split (small shapes) the workspace may be
@@ -106,7 +106,7 @@ typedef enum {
     SQLLM_ERR_NULL = 1,       /* a required pointer is NULL */
     SQLLM_ERR_BITS = 2,       /* bits not 2, 3 or 4 */
     SQLLM_ERR_SHAPE = 3,      /* rows / cols / nnz out of range */
-    SQLLM_ERR_BATCH = 4,      /* batch not in [1, 8] */
+    SQLLM_ERR_BATCH = 4,      /* batch not in [1, 16] */
     SQLLM_ERR_ALIGN = 5,      /* a pointer is not aligned as required */
     SQLLM_ERR_CODE_RANGE = 6, /* sqllm_pack: a code is >= 2^bits */
     SQLLM_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed */
@@ -124,7 +124,8 @@ size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits);
 /* Bytes of workspace the hot calls need for this shape and batch (the same
  * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv):
  * ceil(rows / 64) * 64 * batch * 8, plus at batch >= 5 the transposed x,
- * cols * 16 rounded up to 256; 0 if the arguments are out of range. */
+ * cols * 16 (cols * 32 above batch 8) rounded up to 256; 0 if the arguments
+ * are out of range. */
 size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch);
 
 /*

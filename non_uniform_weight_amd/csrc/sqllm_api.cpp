@@ -108,7 +108,7 @@ int choose_waves(int64_t workgroups)
 // Dense part on the matrix cores: one 4x4x4 step covers 4 columns of 4
 // batch columns where the dot form spends one v_dot2c per pair and batch
 // column (measured faster at every batch, 1 included).
-int use_mf(int batch) { (void)batch; return tuning().dot_only ? 0 : 1; }
+int use_mf(int batch) { return tuning().dot_only && batch <= kMaxDotBatch ? 0 : 1; }
 
 // Stage x in LDS for the outlier gathers when it fits beside the pair table
 // (in half of the LDS when two workgroups share a unit).
@@ -232,7 +232,7 @@ const char *sqllm_status_string(sqllm_status s)
     case SQLLM_ERR_NULL: return "SQLLM_ERR_NULL: required pointer is NULL";
     case SQLLM_ERR_BITS: return "SQLLM_ERR_BITS: bits must be 2, 3 or 4";
     case SQLLM_ERR_SHAPE: return "SQLLM_ERR_SHAPE: rows/cols/nnz out of range";
-    case SQLLM_ERR_BATCH: return "SQLLM_ERR_BATCH: batch must be in [1, 8]";
+    case SQLLM_ERR_BATCH: return "SQLLM_ERR_BATCH: batch must be in [1, 16]";
     case SQLLM_ERR_ALIGN: return "SQLLM_ERR_ALIGN: pointer not aligned as required";
     case SQLLM_ERR_CODE_RANGE: return "SQLLM_ERR_CODE_RANGE: a code is >= 2^bits";
     case SQLLM_ERR_HIP: return "SQLLM_ERR_HIP: HIP runtime or launch failure";

@@ -150,13 +150,14 @@ struct GroupRegs {
 };
 
 // Groups a dense wave keeps in flight, sized so the ring stays within 80
-// (3-bit) or 72 (4-bit, whose table items and lookups need more) of the 128
+// (3-bit), 72 (4-bit, whose table items and lookups need more) or 64 (2-bit,
+// whose replicated table stores need more) of the 128
 // registers a wave has when 16 waves share a compute unit, less 16 per batch
 // quad in the matrix-core form (its accumulators).
 constexpr int ring_depth(int bits, int batch, bool mf)
 {
     const int per = 8 * bits + (mf ? 8 * mf_quads(batch) : 8 * batch);
-    const int d = ((bits <= 3 ? 80 : 72) - (mf ? 16 * mf_quads(batch) : 0)) / per;
+    const int d = ((bits == 2 ? 64 : (bits == 3 ? 80 : 72)) - (mf ? 16 * mf_quads(batch) : 0)) / per;
     return d < 1 ? 1 : (d > 3 ? 3 : d);
 }
 
@@ -425,11 +426,16 @@ __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, false> &r, ui
 // 4h+i.  No activation passes through LDS; the 16 blocks each hold a
 // different 8 columns of x, so one 16-byte register per 128 columns and
 // batch quad serves every step.
+// Accumulator chains per batch quad: two while one or two quads alternate
+// (consecutive matrix steps then never wait on each other's results), one
+// from three quads on (the quads alternate; it saves registers).
+constexpr int mf_chains(int batch) { return mf_quads(batch) >= 3 ? 1 : 2; }
+
 // Step m (columns 4m .. 4m + 3 of the group) of every batch quad; cw holds
 // the table entries of the step's batch of 8 pairs.
 template <int BITS, int B, int M>
 __device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const uint32_t (&cw)[kBatch],
-                                        f32x4 (&macc)[mf_quads(B)][2])
+                                        f32x4 (&macc)[mf_quads(B)][mf_chains(B)])
 {
     constexpr int S = M % 4, sx = M / 32, blk = (M % 32) / 2, part = M % 2;
     const half4_t bv = __builtin_bit_cast(half4_t, u32x2{cw[2 * S], cw[2 * S + 1]});
@@ -437,13 +443,14 @@ __device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const
     for (int h = 0; h < mf_quads(B); ++h) {
         const u32x4 xq = r.xq[2 * h + sx];
         const half4_t av = __builtin_bit_cast(half4_t, part ? u32x2{xq.z, xq.w} : u32x2{xq.x, xq.y});
-        macc[h][S & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, macc[h][S & 1], 4, blk, 0);
+        constexpr int ch = S % mf_chains(B);
+        macc[h][ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, macc[h][ch], 4, blk, 0);
     }
 }
 
 template <int BITS, int B>
 __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, true> &r, uint32_t lane4, const uint32_t *tab,
-                                          f32x4 (&macc)[mf_quads(B)][2])
+                                          f32x4 (&macc)[mf_quads(B)][mf_chains(B)])
 {
     constexpr int NQ = 128 / kBatch; // 16 batches of 8 pairs (16 columns, 4 steps of 4)
     uint32_t wv[2][kBatch];
@@ -530,8 +537,8 @@ __device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it,
 
 // Chunks of 64 nonzeros a wave loads per round: column | fp16 value << 16,
 // one register per chunk, held through the dense steps (fewer where the
-// ring is large).
-constexpr int round_chunks(int bits, int batch) { return bits == 3 && batch == 1 ? 8 : 4; }
+// ring is large, and above batch 8).
+constexpr int round_chunks(int bits, int batch) { return bits == 3 && batch == 1 ? 8 : (batch > 8 ? 2 : 4); }
 
 // Loads of nonzeros [base, base + 64 * R): column and raw fp16 value of one
 // nonzero per lane and chunk, each zero-extended in a register of its own (so
@@ -612,12 +619,23 @@ __device__ __forceinline__ void sparse_gather_t(uint32_t colv, const uint16_t *x
         const u32x2 v = *(const u32x2 *)(xt + (int64_t)colv * 4);
         w[0] = v.x;
         w[1] = v.y;
-    } else {
+    } else if constexpr (P == 8) {
         const u32x4 v = *(const u32x4 *)(xt + (int64_t)colv * 8);
         w[0] = v.x;
         w[1] = v.y;
         w[2] = v.z;
         w[3] = v.w;
+    } else {
+        const u32x4 *p = (const u32x4 *)(xt + (int64_t)colv * 16);
+        const u32x4 v0 = p[0], v1 = p[1];
+        w[0] = v0.x;
+        w[1] = v0.y;
+        w[2] = v0.z;
+        w[3] = v0.w;
+        w[4] = v1.x;
+        w[5] = v1.y;
+        w[6] = v1.z;
+        w[7] = v1.w;
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) xv[b] = (uint16_t)(w[b >> 1] >> (16 * (b & 1)));
@@ -764,9 +782,11 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 #pragma unroll
     for (int k = 0; k < B * NC; ++k) acc[k] = 0.f;
     constexpr int NX = MF ? mf_quads(B) : 1;
-    f32x4 macc[NX][2]; // matrix-core form: [batch quad][chain]
+    f32x4 macc[NX][mf_chains(B)]; // matrix-core form: [batch quad][chain]
 #pragma unroll
-    for (int h = 0; h < NX; ++h) macc[h][0] = macc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NX; ++h)
+#pragma unroll
+        for (int c = 0; c < mf_chains(B); ++c) macc[h][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint32_t *xstage = dyn; // dynamic LDS: x staged for the outlier gathers
 
     // -- 1. the pair-table items beyond ITEMS per thread (workgroups of fewer
@@ -813,9 +833,9 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         }
     };
     auto dense_math = [&](const GroupRegs<BITS, B, MF> &r) {
-        if constexpr (MF)
+        if constexpr (DENSE && MF)
             mac_group<BITS, B>(r, lane4, tab, macc);
-        else
+        else if constexpr (DENSE)
             mac_group<BITS, B>(r, lane4, tab, acc);
     };
     if constexpr (!kRingAfterTable) issue_ring();
@@ -959,7 +979,12 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     if constexpr (MF) {
         // register i of the batch quad h: batch column 4h+i of this lane's row
 #pragma unroll
-        for (int b = 0; b < B; ++b) red[(w * B + b) * 64 + lane] = acc[b] + macc[b / 4][0][b % 4] + macc[b / 4][1][b % 4];
+        for (int b = 0; b < B; ++b) {
+            float v = acc[b];
+#pragma unroll
+            for (int c = 0; c < mf_chains(B); ++c) v += macc[b / 4][c][b % 4];
+            red[(w * B + b) * 64 + lane] = v;
+        }
     } else {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -1037,22 +1062,25 @@ hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream
     return hipGetLastError();
 }
 
-// Batch 1 (and the sparse-only mode) in the dot form; batch >= 2 in the
-// matrix-core form when the shape asks for it.
+// The dense modes in the matrix-core form when the shape asks for it (and
+// always above kMaxDotBatch, where the dot form is not built); the dot form
+// and the outlier-only mode otherwise.
 template <int BITS, int B, int MODE>
 hipError_t launch_group_form(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
     if constexpr (MODE != kSparseAdd)
-        if (ls.mf) return launch_group_one<BITS, B, MODE, true>(g, ls, stream);
-    return launch_group_one<BITS, B, MODE, false>(g, ls, stream);
+        if (ls.mf || B > kMaxDotBatch) return launch_group_one<BITS, B, MODE, true>(g, ls, stream);
+    if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch) return launch_group_one<BITS, B, MODE, false>(g, ls, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int BITS, int B, int MODE>
 hipError_t launch_form(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
     if constexpr (MODE != kSparseAdd)
-        if (ls.mf) return launch_one<BITS, B, MODE, true>(a, ls, stream);
-    return launch_one<BITS, B, MODE, false>(a, ls, stream);
+        if (ls.mf || B > kMaxDotBatch) return launch_one<BITS, B, MODE, true>(a, ls, stream);
+    if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch) return launch_one<BITS, B, MODE, false>(a, ls, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int BITS, int MODE>
@@ -1067,6 +1095,14 @@ hipError_t launch_group_batch(const GroupArgs &g, int batch, const LaunchShape &
     case 6: return launch_group_form<BITS, 6, MODE>(g, ls, stream);
     case 7: return launch_group_form<BITS, 7, MODE>(g, ls, stream);
     case 8: return launch_group_form<BITS, 8, MODE>(g, ls, stream);
+    case 9: return launch_group_form<BITS, 9, MODE>(g, ls, stream);
+    case 10: return launch_group_form<BITS, 10, MODE>(g, ls, stream);
+    case 11: return launch_group_form<BITS, 11, MODE>(g, ls, stream);
+    case 12: return launch_group_form<BITS, 12, MODE>(g, ls, stream);
+    case 13: return launch_group_form<BITS, 13, MODE>(g, ls, stream);
+    case 14: return launch_group_form<BITS, 14, MODE>(g, ls, stream);
+    case 15: return launch_group_form<BITS, 15, MODE>(g, ls, stream);
+    case 16: return launch_group_form<BITS, 16, MODE>(g, ls, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1083,6 +1119,14 @@ hipError_t launch_batch(const KernelArgs &a, int batch, const LaunchShape &ls, h
     case 6: return launch_form<BITS, 6, MODE>(a, ls, stream);
     case 7: return launch_form<BITS, 7, MODE>(a, ls, stream);
     case 8: return launch_form<BITS, 8, MODE>(a, ls, stream);
+    case 9: return launch_form<BITS, 9, MODE>(a, ls, stream);
+    case 10: return launch_form<BITS, 10, MODE>(a, ls, stream);
+    case 11: return launch_form<BITS, 11, MODE>(a, ls, stream);
+    case 12: return launch_form<BITS, 12, MODE>(a, ls, stream);
+    case 13: return launch_form<BITS, 13, MODE>(a, ls, stream);
+    case 14: return launch_form<BITS, 14, MODE>(a, ls, stream);
+    case 15: return launch_form<BITS, 15, MODE>(a, ls, stream);
+    case 16: return launch_form<BITS, 16, MODE>(a, ls, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -11,7 +11,8 @@ namespace sqllm {
 
 constexpr int kTileRows = 64;     // rows per tile = lanes per wave
 constexpr int kGroupCols = 256;   // codes per group
-constexpr int kMaxBatch = 8;
+constexpr int kMaxBatch = 16;
+constexpr int kMaxDotBatch = 8;   // the v_dot2c form is built up to this batch; above it only the matrix cores
 constexpr int kMaxWaves = 16;     // waves per workgroup
 constexpr int kMaxSplit = 64;     // workgroups sharing one row tile
 constexpr int kTableBytes = 256 * 64 * 4;           // pair table: 256 entries x 64 lanes x half2
@@ -91,11 +92,12 @@ inline size_t staged_x_bytes(int64_t cols, int batch) { return (size_t)cols * ba
 
 // x transposed for the outlier gathers from batch kXtBatch on, when the
 // products reading one x carry at least kXtMinNnz nonzeros: all batch
-// columns of a column in one 16-byte word (padded with zeros).  Below that
-// the two extra launches (write, clear) cost more than the gathers save.
+// columns of a column in one 16-byte word (two above batch 8; padded with
+// zeros).  Below that the two extra launches (write, clear) cost more than
+// the gathers save.
 constexpr int kXtBatch = 5;
 constexpr int64_t kXtMinNnz = 400000;
-constexpr int xt_pad(int batch) { return batch <= 2 ? 2 : (batch <= 4 ? 4 : 8); }
+constexpr int xt_pad(int batch) { return batch <= 2 ? 2 : (batch <= 4 ? 4 : (batch <= 8 ? 8 : 16)); }
 inline size_t xt_bytes(int64_t cols, int batch)
 {
     return batch < kXtBatch ? 0 : ((size_t)cols * xt_pad(batch) * 2 + 255) / 256 * 256;

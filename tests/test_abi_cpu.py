@@ -50,7 +50,8 @@ def test_size_queries(nwpkg):
     assert nwpkg.packed_bytes(65, 512, 2) == 2 * 64 * 512 // 4
     assert nwpkg.packed_bytes(64, 256, 1) == 0
     assert nwpkg.workspace_bytes(22016, 8192, 1) >= 344 * 4
-    assert nwpkg.workspace_bytes(22016, 8192, 9) == 0
+    assert nwpkg.workspace_bytes(22016, 8192, 17) == 0
+    assert nwpkg.workspace_bytes(64, 8192, 12) == 12 * 64 * 8 + 8192 * 16 * 2
     # (sum, count) words per output, then at batch >= 5 x transposed to [cols][8]
     assert nwpkg.workspace_bytes(100, 256, 1) == 2 * 64 * 8
     assert nwpkg.workspace_bytes(100, 256, 2) == 2 * 2 * 64 * 8
@@ -89,7 +90,7 @@ def test_gemv_argument_errors(lib):
     assert gemv(lib, cols=0) == 3
     assert gemv(lib, cols=300) == 3
     assert gemv(lib, batch=0) == 4
-    assert gemv(lib, batch=9) == 4
+    assert gemv(lib, batch=17) == 4
     assert gemv(lib, x=MIS) == 5
     assert gemv(lib, x=P(0x200008)) == 5                 # x must be 16-byte aligned
     assert gemv(lib, y=P(0x200001)) == 5
@@ -111,7 +112,7 @@ def test_sparse_argument_errors(lib):
     assert fused(lib, rp=P(0x100002)) == 5
     assert fused(lib, col=P(0x100001)) == 5
     assert spmv(lib, rp=None) == 1
-    assert spmv(lib, batch=9) == 4
+    assert spmv(lib, batch=17) == 4
     assert spmv(lib, cols=65536 + 256) == 3
     assert spmv(lib, x=MIS) == 5
     # no outliers: nothing to do, no HIP call, CSR pointers may be NULL
@@ -148,7 +149,7 @@ def test_group_argument_errors(lib, nwpkg):
     assert group(lib, nwpkg, n=0) == 3
     assert group(lib, nwpkg, n=9) == 3
     assert group(lib, nwpkg, bits=1) == 2
-    assert group(lib, nwpkg, batch=9) == 4
+    assert group(lib, nwpkg, batch=17) == 4
     assert group(lib, nwpkg, packed=None) == 1
     assert group(lib, nwpkg, x=None) == 1
     assert group(lib, nwpkg, row_ptr=None) == 1
@@ -166,7 +167,7 @@ def test_group_workspace_bytes(lib, nwpkg):
     arr = _products(nwpkg, 3, rows=100)
     assert lib.sqllm_group_workspace_bytes(arr, 3, 2) == 3 * nwpkg.workspace_bytes(100, 256, 2)
     assert lib.sqllm_group_workspace_bytes(arr, 0, 1) == 0
-    assert lib.sqllm_group_workspace_bytes(arr, 3, 9) == 0
+    assert lib.sqllm_group_workspace_bytes(arr, 3, 17) == 0
     assert lib.sqllm_group_workspace_bytes(_products(nwpkg, 2, cols=100), 2, 1) == 0
 
 

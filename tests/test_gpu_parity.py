@@ -77,7 +77,7 @@ def test_pack_rejects_out_of_range_code():
 
 # ------------------------------------------------------------ products, small shapes
 
-SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8), (300, 4096, 1)]
+SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8), (300, 4096, 1), (129, 1024, 16)]
 SPARSITY = ["none", "one", "5pct", "50pct", "full", "empty_rows", "dense_row"]
 
 
@@ -340,6 +340,30 @@ def test_dense_forms_every_batch(bits, batch, form):
         assert_close(yg, yd_ref, dscale, TOL, f"gemv waves={waves}")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("batch", [9, 12, 16])
+def test_matrix_form_above_batch_8(bits, batch):
+    """Batches 9-16 (matrix-core form only: three or four batch quads on the
+    same weight operand), fused and dense-only, 16 / 8 / 3 waves."""
+    rng = np.random.default_rng(stable_seed(bits, batch, "above-8"))
+    rows, cols = 193, 4096
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "5pct")
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    yd_ref, dscale = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    for waves in (16, 8, 3):
+        step(f"matrix form bits={bits} batch={batch} waves={waves}")
+        try:
+            nw().set_tuning(waves=waves)
+            y = d.fused()
+            yg = d.gemv()
+            torch.cuda.synchronize()
+        finally:
+            nw().set_tuning()
+        assert_close(y, y_ref, scale, TOL, f"fused waves={waves}")
+        assert_close(yg, yd_ref, dscale, TOL, f"gemv waves={waves}")
+
+
 # ------------------------------------------------------------ the evaluation workloads
 
 def _check_matrix(m: synth.Matrix, sel=None, ws=None):
@@ -363,7 +387,7 @@ def test_workload_full(workload):
         _check_matrix(m)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8, 16])
 def test_workload4(batch):
     rng = np.random.default_rng(batch)
     for i, spec in enumerate(synth.workload(4, batch=batch)):
@@ -438,7 +462,7 @@ GROUP_CASES = [(193, 4096, "5pct"), (64, 256, "none"), (1000, 2048, "empty_rows"
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("batch", [1, 3, 8, 16])
 def test_group_matches_oracle(bits, batch):
     """Products of different shapes, with and without outliers (two launches),
     ragged row tails: each output within tolerance of the oracle."""
@@ -507,7 +531,7 @@ def test_one_workspace_many_shapes():
     carry over 400K nonzeros) it is all zero again."""
     rng = np.random.default_rng(stable_seed("ws-many"))
     seq = [(300, 4096, 8, "50pct"), (1000, 2048, 1, "5pct"), (64, 8192, 6, "full"), (2000, 256, 2, "one"),
-           (129, 4096, 3, "dense_row")]
+           (129, 4096, 3, "dense_row"), (200, 4096, 16, "50pct")]
     need = max(nw().workspace_bytes(r, c, b) for r, c, b, _ in seq)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for rows, cols, batch, sp in seq + seq[::-1]:
@@ -525,7 +549,7 @@ def test_one_workspace_many_shapes():
         assert int(ws.count_nonzero().item()) == 0
 
 
-@pytest.mark.parametrize("batch", [5, 8])
+@pytest.mark.parametrize("batch", [5, 8, 16])
 def test_outliers_without_room_for_transposed_x(batch):
     """A workspace that holds only the (sum, count) words: the outliers read
     x in place; with the full workspace they read the transposed copy (526K
