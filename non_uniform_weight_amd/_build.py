@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsqllm.so")
 
 SOURCES = ["sqllm_fused2.hip", "sqllm_gemv2.hip", "sqllm_fused3.hip", "sqllm_fused4.hip", "sqllm_gemv3.hip",
-           "sqllm_gemv4.hip", "sqllm_sparse.hip", "sqllm_pack.hip", "sqllm_quantize.hip", "sqllm_api.cpp"]
+           "sqllm_gemv4.hip", "sqllm_wide2.hip", "sqllm_wide3.hip", "sqllm_wide4.hip", "sqllm_sparse.hip",
+           "sqllm_pack.hip", "sqllm_quantize.hip", "sqllm_api.cpp"]
 OBJDIR = os.path.join(PKG, "_build")
 
 # gfx950 only; packed fp32 instructions are switched off (the device pass

@@ -435,7 +435,7 @@ constexpr int mf_chains(int batch) { return mf_quads(batch) >= 3 ? 1 : 2; }
 // the table entries of the step's batch of 8 pairs.
 template <int BITS, int B, int M>
 __device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const uint32_t (&cw)[kBatch],
-                                        f32x4 (&macc)[mf_quads(B)][mf_chains(B)])
+                                        f32x4 (&macc)[mf_quads(B)][2])
 {
     constexpr int S = M % 4, sx = M / 32, blk = (M % 32) / 2, part = M % 2;
     const half4_t bv = __builtin_bit_cast(half4_t, u32x2{cw[2 * S], cw[2 * S + 1]});
@@ -443,14 +443,14 @@ __device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const
     for (int h = 0; h < mf_quads(B); ++h) {
         const u32x4 xq = r.xq[2 * h + sx];
         const half4_t av = __builtin_bit_cast(half4_t, part ? u32x2{xq.z, xq.w} : u32x2{xq.x, xq.y});
-        constexpr int ch = S % mf_chains(B);
-        macc[h][ch] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, macc[h][ch], 4, blk, 0);
+        macc[h][mf_chains(B) == 2 ? (S & 1) : 0] =
+            __builtin_amdgcn_mfma_f32_4x4x4f16(av, bv, macc[h][mf_chains(B) == 2 ? (S & 1) : 0], 4, blk, 0);
     }
 }
 
 template <int BITS, int B>
 __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, true> &r, uint32_t lane4, const uint32_t *tab,
-                                          f32x4 (&macc)[mf_quads(B)][mf_chains(B)])
+                                          f32x4 (&macc)[mf_quads(B)][2])
 {
     constexpr int NQ = 128 / kBatch; // 16 batches of 8 pairs (16 columns, 4 steps of 4)
     uint32_t wv[2][kBatch];
@@ -782,11 +782,9 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 #pragma unroll
     for (int k = 0; k < B * NC; ++k) acc[k] = 0.f;
     constexpr int NX = MF ? mf_quads(B) : 1;
-    f32x4 macc[NX][mf_chains(B)]; // matrix-core form: [batch quad][chain]
+    f32x4 macc[NX][2]; // matrix-core form: [batch quad][chain] (chain 1 unused from three quads on)
 #pragma unroll
-    for (int h = 0; h < NX; ++h)
-#pragma unroll
-        for (int c = 0; c < mf_chains(B); ++c) macc[h][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < NX; ++h) macc[h][0] = macc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint32_t *xstage = dyn; // dynamic LDS: x staged for the outlier gathers
 
     // -- 1. the pair-table items beyond ITEMS per thread (workgroups of fewer
@@ -980,10 +978,10 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         // register i of the batch quad h: batch column 4h+i of this lane's row
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            float v = acc[b];
-#pragma unroll
-            for (int c = 0; c < mf_chains(B); ++c) v += macc[b / 4][c][b % 4];
-            red[(w * B + b) * 64 + lane] = v;
+            if constexpr (mf_chains(B) == 2)
+                red[(w * B + b) * 64 + lane] = acc[b] + macc[b / 4][0][b % 4] + macc[b / 4][1][b % 4];
+            else
+                red[(w * B + b) * 64 + lane] = acc[b] + macc[b / 4][0][b % 4];
         }
     } else {
 #pragma unroll
@@ -1083,52 +1081,28 @@ hipError_t launch_form(const KernelArgs &a, const LaunchShape &ls, hipStream_t s
     return hipErrorInvalidValue;
 }
 
-template <int BITS, int MODE>
+// Batches LO..HI of one (bits, mode).  The batch-1..8 kernels and the
+// batch-9..16 ones are instantiated in separate translation units: sharing
+// one unit changes the compiler's code for the small batches (measured 6%
+// slower at batch 1).
+template <int BITS, int MODE, int LO, int HI>
 hipError_t launch_group_batch(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    switch (batch) {
-    case 1: return launch_group_form<BITS, 1, MODE>(g, ls, stream);
-    case 2: return launch_group_form<BITS, 2, MODE>(g, ls, stream);
-    case 3: return launch_group_form<BITS, 3, MODE>(g, ls, stream);
-    case 4: return launch_group_form<BITS, 4, MODE>(g, ls, stream);
-    case 5: return launch_group_form<BITS, 5, MODE>(g, ls, stream);
-    case 6: return launch_group_form<BITS, 6, MODE>(g, ls, stream);
-    case 7: return launch_group_form<BITS, 7, MODE>(g, ls, stream);
-    case 8: return launch_group_form<BITS, 8, MODE>(g, ls, stream);
-    case 9: return launch_group_form<BITS, 9, MODE>(g, ls, stream);
-    case 10: return launch_group_form<BITS, 10, MODE>(g, ls, stream);
-    case 11: return launch_group_form<BITS, 11, MODE>(g, ls, stream);
-    case 12: return launch_group_form<BITS, 12, MODE>(g, ls, stream);
-    case 13: return launch_group_form<BITS, 13, MODE>(g, ls, stream);
-    case 14: return launch_group_form<BITS, 14, MODE>(g, ls, stream);
-    case 15: return launch_group_form<BITS, 15, MODE>(g, ls, stream);
-    case 16: return launch_group_form<BITS, 16, MODE>(g, ls, stream);
-    default: return hipErrorInvalidValue;
-    }
+    hipError_t r = hipErrorInvalidValue;
+    [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+        ((batch == LO + Ks ? (void)(r = launch_group_form<BITS, LO + Ks, MODE>(g, ls, stream)) : void()), ...);
+    }(std::make_integer_sequence<int, HI - LO + 1>{});
+    return r;
 }
 
-template <int BITS, int MODE>
+template <int BITS, int MODE, int LO, int HI>
 hipError_t launch_batch(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    switch (batch) {
-    case 1: return launch_form<BITS, 1, MODE>(a, ls, stream);
-    case 2: return launch_form<BITS, 2, MODE>(a, ls, stream);
-    case 3: return launch_form<BITS, 3, MODE>(a, ls, stream);
-    case 4: return launch_form<BITS, 4, MODE>(a, ls, stream);
-    case 5: return launch_form<BITS, 5, MODE>(a, ls, stream);
-    case 6: return launch_form<BITS, 6, MODE>(a, ls, stream);
-    case 7: return launch_form<BITS, 7, MODE>(a, ls, stream);
-    case 8: return launch_form<BITS, 8, MODE>(a, ls, stream);
-    case 9: return launch_form<BITS, 9, MODE>(a, ls, stream);
-    case 10: return launch_form<BITS, 10, MODE>(a, ls, stream);
-    case 11: return launch_form<BITS, 11, MODE>(a, ls, stream);
-    case 12: return launch_form<BITS, 12, MODE>(a, ls, stream);
-    case 13: return launch_form<BITS, 13, MODE>(a, ls, stream);
-    case 14: return launch_form<BITS, 14, MODE>(a, ls, stream);
-    case 15: return launch_form<BITS, 15, MODE>(a, ls, stream);
-    case 16: return launch_form<BITS, 16, MODE>(a, ls, stream);
-    default: return hipErrorInvalidValue;
-    }
+    hipError_t r = hipErrorInvalidValue;
+    [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+        ((batch == LO + Ks ? (void)(r = launch_form<BITS, LO + Ks, MODE>(a, ls, stream)) : void()), ...);
+    }(std::make_integer_sequence<int, HI - LO + 1>{});
+    return r;
 }
 
 } // namespace dev

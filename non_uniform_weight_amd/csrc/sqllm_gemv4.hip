@@ -5,12 +5,12 @@ namespace sqllm {
 
 hipError_t launch_gemv4(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    return dev::launch_batch<4, kDenseOnly>(a, batch, ls, stream);
+    return dev::launch_batch<4, kDenseOnly, 1, kMaxDotBatch>(a, batch, ls, stream);
 }
 
 hipError_t launch_group_gemv4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    return dev::launch_group_batch<4, kDenseOnly>(g, batch, ls, stream);
+    return dev::launch_group_batch<4, kDenseOnly, 1, kMaxDotBatch>(g, batch, ls, stream);
 }
 
 } // namespace sqllm

@@ -28,18 +28,37 @@ hipError_t launch_group_fused3(const GroupArgs &g, int batch, const LaunchShape 
 hipError_t launch_group_fused4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_group_gemv3(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_group_gemv4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+#define SQLLM_WIDE(bits)                                                                                              \
+    hipError_t launch_fused##bits##_wide(const KernelArgs &, int, const LaunchShape &, hipStream_t);                  \
+    hipError_t launch_gemv##bits##_wide(const KernelArgs &, int, const LaunchShape &, hipStream_t);                   \
+    hipError_t launch_group_fused##bits##_wide(const GroupArgs &, int, const LaunchShape &, hipStream_t);             \
+    hipError_t launch_group_gemv##bits##_wide(const GroupArgs &, int, const LaunchShape &, hipStream_t);
+SQLLM_WIDE(2)
+SQLLM_WIDE(3)
+SQLLM_WIDE(4)
+#undef SQLLM_WIDE
+hipError_t launch_spmv_add_wide(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
                                hipStream_t stream)
 {
+    const bool wide = batch > kMaxDotBatch;
     switch (mode) {
     case kFused:
+        if (wide)
+            return bits == 2   ? launch_fused2_wide(a, batch, ls, stream)
+                   : bits == 3 ? launch_fused3_wide(a, batch, ls, stream)
+                               : launch_fused4_wide(a, batch, ls, stream);
         return bits == 2 ? launch_fused2(a, batch, ls, stream)
                          : bits == 3 ? launch_fused3(a, batch, ls, stream) : launch_fused4(a, batch, ls, stream);
     case kDenseOnly:
+        if (wide)
+            return bits == 2   ? launch_gemv2_wide(a, batch, ls, stream)
+                   : bits == 3 ? launch_gemv3_wide(a, batch, ls, stream)
+                               : launch_gemv4_wide(a, batch, ls, stream);
         return bits == 2 ? launch_gemv2(a, batch, ls, stream)
                          : bits == 3 ? launch_gemv3(a, batch, ls, stream) : launch_gemv4(a, batch, ls, stream);
-    case kSparseAdd: return launch_spmv_add(a, batch, ls, stream);
+    case kSparseAdd: return wide ? launch_spmv_add_wide(a, batch, ls, stream) : launch_spmv_add(a, batch, ls, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -47,12 +66,21 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
 hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mode mode, const LaunchShape &ls,
                                      hipStream_t stream)
 {
+    const bool wide = batch > kMaxDotBatch;
     switch (mode) {
     case kFused:
+        if (wide)
+            return bits == 2   ? launch_group_fused2_wide(g, batch, ls, stream)
+                   : bits == 3 ? launch_group_fused3_wide(g, batch, ls, stream)
+                               : launch_group_fused4_wide(g, batch, ls, stream);
         return bits == 2   ? launch_group_fused2(g, batch, ls, stream)
                : bits == 3 ? launch_group_fused3(g, batch, ls, stream)
                            : launch_group_fused4(g, batch, ls, stream);
     case kDenseOnly:
+        if (wide)
+            return bits == 2   ? launch_group_gemv2_wide(g, batch, ls, stream)
+                   : bits == 3 ? launch_group_gemv3_wide(g, batch, ls, stream)
+                               : launch_group_gemv4_wide(g, batch, ls, stream);
         return bits == 2   ? launch_group_gemv2(g, batch, ls, stream)
                : bits == 3 ? launch_group_gemv3(g, batch, ls, stream)
                            : launch_group_gemv4(g, batch, ls, stream);

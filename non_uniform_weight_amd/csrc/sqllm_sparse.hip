@@ -5,7 +5,7 @@ namespace sqllm {
 
 hipError_t launch_spmv_add(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
-    return dev::launch_batch<3, kSparseAdd>(a, batch, ls, stream);
+    return dev::launch_batch<3, kSparseAdd, 1, kMaxDotBatch>(a, batch, ls, stream);
 }
 
 } // namespace sqllm
