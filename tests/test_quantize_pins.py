@@ -161,3 +161,35 @@ def test_zero_sensitivity_weights_take_no_part():
     c_all = q.kmeans_row(x, wt, 8, 15)
     c_sub = q.kmeans_row(x[keep], wt[keep], 8, 15)
     assert np.allclose(c_all, c_sub, rtol=1e-12, atol=0)
+
+
+def test_kmeans_ties_go_to_the_lower_centroid():
+    """A weight halfway between two centroids takes the lower one, in the
+    assignment steps and in the final codes.  Row 0, 0.5, 3 at 2 bits with no
+    steps: the centroids stay at the uniform start 0, 1, 2, 3."""
+    assert int(q.nearest(np.array([0.5]), np.array([0.0, 1.0]))[0]) == 0
+    row = f16([0.0, 0.5, 3.0]).reshape(1, 3)
+    codes, lut = q.kmeans_lut(row, None, 2, 0)
+    assert np.array_equal(q.f16_to_f64(lut[0]), [0.0, 1.0, 2.0, 3.0])
+    assert codes[0].tolist() == [0, 0, 3]
+
+
+def test_kmeans_codes_are_nearest_to_the_fp16_table():
+    """Codes follow the stored fp16 table, not the fp64 centroids.  Row 0,
+    1001.5, 6008 at 2 bits with no steps: centroid 1 is 6008/3 = 2002.67,
+    stored as 2003, so 1001.5 sits exactly halfway between 0 and 2003 (tie:
+    code 0), while against 2002.67 it would be nearer code 1."""
+    row = f16([0.0, 1001.5, 6008.0]).reshape(1, 3)
+    codes, lut = q.kmeans_lut(row, None, 2, 0)
+    assert q.f16_to_f64(lut[0])[1] == 2003.0
+    assert codes[0].tolist() == [0, 0, 3]
+
+
+def test_objective_weighs_each_error_by_its_sensitivity():
+    """Eq. 6: sum of F_i (w_i - Q(w_i))^2, by hand: weights 1 and 2 both coded
+    to centroid 0 with sensitivities 3 and 5 -> 3*1 + 5*4 = 23."""
+    d = f16([1.0, 2.0]).reshape(1, 2)
+    lut = f16([0.0, 10.0, 20.0, 30.0]).reshape(1, 4)
+    codes = np.zeros((1, 2), np.uint8)
+    assert q.objective(d, np.array([[3.0, 5.0]]), codes, lut)[0] == 23.0
+    assert q.objective(d, None, codes, lut)[0] == 5.0
