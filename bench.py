@@ -55,11 +55,12 @@ def parse():
                    help="level: one group launch per (q,k,v), (o), (gate,up), (down); single: one call per product")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
-    p.add_argument("--ablation", choices=("outliers", "batch", "offline"), default=None,
+    p.add_argument("--ablation", choices=("outliers", "batch", "offline", "configs"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
                         "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8, 16 in both dense forms; offline: the "
-                        "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample")
+                        "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample; configs: "
+                        "every matrix of the 7B, 7B-MLP, 13B and 65B single-matrix workloads, cold and warm")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
     return p.parse_args()
@@ -370,6 +371,117 @@ def batch_ablation(args) -> None:
           flush=True)
 
 
+def config_table(args) -> None:
+    """Each matrix of the four single-matrix workloads, one fused call per
+    product: the 7B q_proj 4096x4096 (3-bit), the 7B MLP pair up 11008x4096 +
+    down 4096x11008 (4-bit), the 13B layer's seven linears (3-bit, Zipf rows)
+    and the three 65B shapes at batch 1, 2, 4 and 8 (3-bit), all with 0.45%
+    outliers.  Cold: every call reads its own copy of codes, tables and CSR
+    (copies >= 1 GB, beyond the caches), 200 calls per trial, median of 5
+    trials, as a HIP graph and as a plain launch loop (arguments marshalled
+    once, one C-ABI call per product).  Warm: 200 graph calls on one copy
+    (cache-resident for the smaller shapes, reported apart)."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import non_uniform_weight_amd as nw
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    h = vp_stream(stream)
+    fn = nw.library().sqllm_dense_sparse_gemv
+    vp = ctypes.c_void_p
+    calls_per_trial, trials = 200, 5
+    cases = [(1, s) for s in synth.workload(1)] + [(2, s) for s in synth.workload(2)]
+    cases += [(3, s) for s in synth.workload(3)]
+    cases += [(4, s) for b in (1, 2, 4, 8) for s in synth.workload(4, batch=b)]
+    out = []
+    for wl, spec in cases:
+        index = [s.name for s in synth.workload(wl, batch=spec.batch)].index(spec.name)
+        m = synth.make_matrix(spec, seed=args.seed, workload=wl, index=index)
+        packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
+        lut = torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16)
+        rp = torch.from_numpy(m.row_ptr).cuda()
+        col = torch.from_numpy(m.col.view(np.int16)).cuda()
+        val = torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16)
+        x = torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16)
+        y = torch.empty((spec.batch, spec.rows), dtype=torch.float16, device="cuda")
+        ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, spec.batch), 256), dtype=torch.uint8,
+                         device="cuda")
+        nnz = int(m.col.size)
+        nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, nnz, spec.batch)
+        reps = max(1, -(-1024 * 2 ** 20 // nbytes))
+        copies = [(packed, lut, rp, col, val)] + [tuple(t.clone() for t in (packed, lut, rp, col, val))
+                                                  for _ in range(reps - 1)]
+        argv = [(vp(c[0].data_ptr()), vp(c[1].data_ptr()), spec.bits, vp(c[2].data_ptr()), vp(c[3].data_ptr()),
+                 vp(c[4].data_ptr()), nnz, spec.rows, spec.cols, vp(x.data_ptr()), spec.batch, vp(y.data_ptr()),
+                 vp(ws.data_ptr()), ws.numel()) for c in copies]
+
+        def run(k, cold=True):
+            st = fn(*argv[k % reps if cold else 0], h)
+            if st != 0:
+                raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
+
+        def graph_us(cold):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for k in range(calls_per_trial):
+                    run(k, cold)
+            ts = []
+            with torch.cuda.stream(stream):
+                g.replay()  # warm-up: 200 calls
+                torch.cuda.synchronize()
+                for _ in range(trials):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    g.replay()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
+            del g
+            return statistics.median(ts)
+
+        def plain_us():
+            ts = []
+            with torch.cuda.stream(stream):
+                for k in range(20):
+                    run(k)
+                torch.cuda.synchronize()
+                for _ in range(trials):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for k in range(calls_per_trial):
+                        run(k)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
+            return statistics.median(ts)
+
+        cold, plain, warm = graph_us(True), plain_us(), graph_us(False)
+        ideal = nbytes / (HBM_PEAK_GBS * 1e3)
+        res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "bits": spec.bits,
+               "batch": spec.batch, "nnz": nnz, "bytes": nbytes, "copies": reps,
+               "ideal_us": round(ideal, 3), "target70_us": round(ideal / 0.7, 3),
+               "graph_us": round(cold, 3), "GB_per_s": round(nbytes / (cold * 1e3), 1),
+               "pct_peak": round(100 * ideal / cold, 1), "plain_us": round(plain, 3),
+               "warm_us": round(warm, 3), "warm_GB_per_s": round(nbytes / (warm * 1e3), 1)}
+        log(f"config {res}")
+        out.append(res)
+        del copies, argv, packed, lut, rp, col, val
+        torch.cuda.empty_cache()
+    totals = {}
+    for wl, name in ((2, "mlp_pair"), (3, "layer")):
+        sel = [r for r in out if r["workload"] == wl]
+        us = sum(r["graph_us"] for r in sel)
+        totals[f"workload{wl}_{name}"] = {"graph_us": round(us, 3), "GB_per_s": round(
+            sum(r["bytes"] for r in sel) / (us * 1e3), 1)}
+    print(json.dumps({"ablation": "configs", "unit": "us per product (median of 5 trials of 200 calls)",
+                      "products": out, "totals": totals}), flush=True)
+
+
 def offline_ablation(args) -> None:
     """The offline steps on the three LLaMA-65B shapes: thresholds (0.2 / 99.8
     percentiles and the 0.05% most sensitive), CSR + D extraction, and 3-bit
@@ -455,6 +567,9 @@ def main():
         return
     if args.ablation == "offline":
         offline_ablation(args)
+        return
+    if args.ablation == "configs":
+        config_table(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "

@@ -59,7 +59,7 @@ sqllm_status check_shape(int64_t rows, int64_t cols)
 }
 
 // One 8-byte (fp32 sum, count) word per (tile, batch column, row of tile),
-// then (batch >= 2) x transposed for the outlier gathers.
+// then (from batch kXtBatch) x transposed for the outlier gathers.
 size_t slots_need(int64_t rows, int batch)
 {
     return (size_t)tiles_of(rows) * (size_t)batch * kTileRows * 8;
@@ -74,8 +74,11 @@ bool wants_xt(const KernelArgs &a, int batch, int64_t nnz) { return batch >= kXt
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Column split and waves for the dense modes: about target_wgs workgroups,
-// at least min_gps groups each.  With
+// Column split and waves for the dense modes: at most target_wgs workgroups
+// (one per compute unit; a few more leave a tail in which some units run two
+// workgroups: 11008x4096 at split 2, 344 workgroups, measured 10.8 us against
+// 8.3 at split 1), one split more only when fewer than 60% of the units would
+// be busy, and at least min_gps groups per workgroup.  With
 // outliers x is staged in LDS when it fits beside the pair table -- for two
 // workgroups per compute unit when there are more workgroups than units.
 // total_tiles: row tiles of every product sharing the launch.
@@ -84,7 +87,10 @@ void choose_split(KernelArgs &a, int64_t total_tiles)
     const int64_t G = a.groups;
     int64_t s = tuning().force_split;
     if (s <= 0) {
-        s = ceil_div(tuning().target_wgs, total_tiles);
+        const int64_t t = tuning().target_wgs;
+        s = t / total_tiles;
+        if (s < 1) s = 1;
+        if (total_tiles * s * 5 < t * 3) ++s;
         int64_t cap = G / tuning().min_gps;
         if (cap < 1) cap = 1;
         if (s > cap) s = cap;
@@ -98,15 +104,16 @@ void choose_split(KernelArgs &a, int64_t total_tiles)
 }
 
 // More workgroups than units: 8 waves, two workgroups per unit.  One
-// workgroup per unit: up to 16 waves, but at least two column groups per
-// wave so that its ring of loads overlaps (8192x8192: 16 groups per
-// workgroup -> 8 waves, measured 7% faster than 16 waves of one group).
+// workgroup per unit: 8 waves up to 16 column groups (two groups per wave,
+// so that a wave's ring of loads overlaps: 8192x8192 at 16 groups per
+// workgroup measured 7% faster than 16 waves of one group), 12 waves up to
+// 32 groups (13824x5120 at 20 groups: 9.7 us against 10.2 at 10 waves and
+// 10.6 at 16), 16 beyond.
 int choose_waves(int64_t workgroups, int gps)
 {
     if (tuning().force_waves) return tuning().force_waves;
-    if (workgroups > tuning().target_wgs) return kDefaultWaves;
-    const int w = gps / 2;
-    return w < kDefaultWaves ? kDefaultWaves : (w > kMaxWaves ? kMaxWaves : w);
+    if (workgroups > tuning().target_wgs || gps <= 16) return kDefaultWaves;
+    return gps <= 32 ? 12 : kMaxWaves;
 }
 
 // Dense part on the matrix cores: one 4x4x4 step covers 4 columns of 4

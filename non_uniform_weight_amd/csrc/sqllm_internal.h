@@ -47,14 +47,14 @@ struct GroupArgs {
     KernelArgs item[kMaxGroup];
 };
 
-// Matrix-core form of the dense part (batch >= 2): batch columns in quads of 4.
+// Matrix-core form of the dense part: batch columns in quads of 4.
 constexpr int mf_quads(int batch) { return (batch + 3) / 4; }
 
 // One launch configuration, chosen on the host.
 struct LaunchShape {
     int waves;                // waves per workgroup
     size_t dyn_lds;           // dynamic LDS bytes (staged x)
-    int mf;                   // 1: dense part on the matrix cores (batch >= 2)
+    int mf;                   // 1: dense part on the matrix cores, 0: dot form (batch <= kMaxDotBatch)
 };
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,

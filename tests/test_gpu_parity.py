@@ -291,7 +291,7 @@ def test_workspace_shared_across_shapes():
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("split,waves", [(1, 1), (1, 16), (2, 8), (3, 5), (7, 2), (16, 1), (0, 0)])
+@pytest.mark.parametrize("split,waves", [(1, 1), (1, 12), (1, 16), (2, 8), (3, 5), (3, 12), (7, 2), (16, 1), (0, 0)])
 def test_launch_configurations(bits, split, waves):
     """Column splits and waves per workgroup of every kind give the same
     answer (one wave per workgroup included)."""
