@@ -116,6 +116,33 @@ int choose_waves(int64_t workgroups, int gps)
     return gps <= 32 ? 12 : kMaxWaves;
 }
 
+// A group launch of more tiles than compute units but at most two per unit
+// runs two 8-wave workgroups per unit, and at split 1 some units get two
+// whole tiles while others get one.  Leading products then go to split 2
+// while the launch stays within two workgroups per unit: their half tiles
+// are dispatched first and take one slot of every unit, the whole tiles the
+// other (q, k, v of 8192x8192, 384 tiles: q at split 2 gives 512
+// workgroups, 19.6 us against 21.1 at split 1; splitting the last product
+// instead, or (gate, up) at 688 tiles in any mix, measured slower).
+// Returns the launch's workgroup count.
+int64_t fill_two_slots(GroupArgs &g, int64_t wgs, void *const *own_ws, const size_t *own_bytes, int batch)
+{
+    const int64_t t = tuning().target_wgs;
+    if (tuning().force_split || tuning().force_waves || wgs <= t || wgs >= 2 * t) return wgs;
+    for (int k = 0; k < g.n; ++k)
+        if (g.item[k].split != 1) return wgs;
+    for (int k = 0; k < g.n; ++k) {
+        KernelArgs &a = g.item[k];
+        if (wgs + a.tiles > 2 * t || a.groups < 2 * tuning().min_gps) break;
+        if (!own_ws[k] || own_bytes[k] < slots_need(a.rows, batch)) break;
+        a.gps = (int)ceil_div(a.groups, 2);
+        a.split = (int)ceil_div(a.groups, a.gps);
+        wgs += (int64_t)a.tiles * (a.split - 1);
+        if ((int64_t)a.tiles * a.split > g.wgs) g.wgs = a.tiles * a.split;
+    }
+    return wgs;
+}
+
 // Dense part on the matrix cores: one 4x4x4 step covers 4 columns of 4
 // batch columns where the dot form spends one v_dot2c per pair and batch
 // column (measured faster at every batch, 1 included).
@@ -420,6 +447,7 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
             ++g.n;
         }
         if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
+        wgs = fill_two_slots(g, wgs, own_ws, own_bytes, batch);
         LaunchShape ls{};
         ls.mf = use_mf(batch);
         int max_gps = 1;
