@@ -143,6 +143,42 @@ int64_t fill_two_slots(GroupArgs &g, int64_t wgs, void *const *own_ws, const siz
     return wgs;
 }
 
+// The same for one product of more tiles than compute units but fewer than
+// twice as many: it runs as two row slices in one group launch, the first h
+// tiles at split 2 and the rest whole, h chosen so that the launch has two
+// workgroups per unit (22016x8192, 344 tiles: 168 tiles at split 2 and 176
+// whole, where at split 1 the 88 units that run two whole tiles end long
+// after the others).  The slices share x, the outliers' arrays, the
+// transposed x and the workspace (only the first slice uses its words).
+// False when the launch shape is forced or the workspace lacks the words.
+bool slice_for_two_slots(const KernelArgs &a, int bits, int batch, void *ws, size_t ws_bytes, GroupArgs &g)
+{
+    const int64_t t = tuning().target_wgs;
+    if (tuning().force_split || tuning().force_waves || a.split != 1 || a.tiles <= t || a.tiles >= 2 * t) return false;
+    const int h = (int)(2 * t - a.tiles);
+    if (a.groups < 2 * tuning().min_gps) return false;
+    if (!ws || !aligned(ws, 256) || ws_bytes < slots_need((int64_t)h * kTileRows, batch)) return false;
+    const int64_t r0 = (int64_t)h * kTileRows;
+    KernelArgs lo = a, hi = a;
+    lo.rows = (int)r0;
+    lo.tiles = h;
+    lo.gps = (int)ceil_div(a.groups, 2);
+    lo.split = (int)ceil_div(a.groups, lo.gps);
+    hi.rows = a.rows - (int)r0;
+    hi.tiles = a.tiles - h;
+    hi.packed = (const char *)a.packed + r0 * a.cols * bits / 8; // tile-major codes: whole tiles precede
+    hi.lut = a.lut + r0 * (1 << bits);
+    if (a.row_ptr) hi.row_ptr = a.row_ptr + r0; // absolute offsets into col / val
+    hi.y = a.y + r0;                            // ldy stays the whole product's row count
+    hi.slots = nullptr;
+    g = GroupArgs{};
+    g.n = 2;
+    g.item[0] = lo;
+    g.item[1] = hi;
+    g.wgs = lo.tiles * lo.split > hi.tiles ? lo.tiles * lo.split : hi.tiles;
+    return true;
+}
+
 // Dense part on the matrix cores: one 4x4x4 step covers 4 columns of 4
 // batch columns where the dot form spends one v_dot2c per pair and batch
 // column (measured faster at every batch, 1 included).
@@ -252,6 +288,7 @@ KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y,
     a.y = y;
     a.slots = (unsigned long long *)ws;
     a.rows = (int)rows;
+    a.ldy = (int)rows;
     a.cols = (int)cols;
     a.tiles = (int)tiles_of(rows);
     a.groups = (int)(cols / kGroupCols);
@@ -344,8 +381,13 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     if (st != SQLLM_OK) return st;
     XtJobs jobs{};
     plan_xt(a, batch, nnz, nnz, workspace, workspace_bytes, jobs);
+    const Mode mode = nnz > 0 ? kFused : kDenseOnly;
+    GroupArgs g;
+    const bool sliced = slice_for_two_slots(a, bits, batch, workspace, workspace_bytes, g);
+    if (sliced) ls.waves = choose_waves((int64_t)g.item[0].tiles * g.item[0].split + g.item[1].tiles, g.item[0].gps);
     if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
-        launch_dense_sparse(a, bits, batch, nnz > 0 ? kFused : kDenseOnly, ls, stream) != hipSuccess ||
+        (sliced ? launch_dense_sparse_group(g, bits, batch, mode, ls, stream)
+                : launch_dense_sparse(a, bits, batch, mode, ls, stream)) != hipSuccess ||
         launch_xt_clear(jobs, batch, stream) != hipSuccess)
         return SQLLM_ERR_HIP;
     return SQLLM_OK;

@@ -699,8 +699,8 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 float v = tot[b];
-                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.rows + row]);
-                a.y[(int64_t)b * a.rows + row] = f32_to_f16_rne(v);
+                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
+                a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
             }
         }
         return;
@@ -723,8 +723,8 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
         if ((int)(desired >> 32) == count) {
             if (row < a.rows) {
                 float v = __uint_as_float((uint32_t)desired);
-                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.rows + row]);
-                a.y[(int64_t)b * a.rows + row] = f32_to_f16_rne(v);
+                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
+                a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
             }
             __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -751,7 +751,7 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane
 __device__ __forceinline__ void load_args_now(const KernelArgs &a)
 {
     asm volatile("" ::"s"(a.packed), "s"(a.lut), "s"(a.row_ptr), "s"(a.col), "s"(a.val), "s"(a.x), "s"(a.y),
-                 "s"(a.slots), "s"(a.rows), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
+                 "s"(a.slots), "s"(a.rows), "s"(a.ldy), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
                  "s"(a.x_lds), "s"(a.xt), "s"(a.sparse_naive), "s"(blockDim.x));
 }
 

@@ -32,6 +32,7 @@ struct KernelArgs {
     uint16_t *y;              // fp16 [batch][rows]
     unsigned long long *slots;  // workspace: one (fp32 sum, count) word per (tile, batch, row)
     int rows, cols, tiles, groups;
+    int ldy;                  // y's batch stride: rows, or more for a row slice of a larger product
     int split;                // workgroups per row tile
     int gps;                  // column groups per workgroup (the last one may have fewer)
     int x_lds;                // 1: all of x staged in LDS for the outlier gathers

@@ -498,6 +498,50 @@ def test_group_equals_single_calls(split):
         assert np.array_equal(dev_to_u16(y), dev_to_u16(ys_)), f"group item {shape} differs from the single call"
 
 
+@pytest.mark.parametrize("bits,batch,sparsity", [(3, 1, "5pct"), (3, 3, "dense_row"), (4, 6, "50pct"),
+                                                   (2, 2, "none"), (3, 16, "5pct")])
+def test_row_slices_for_two_slots(bits, batch, sparsity):
+    """A product of more row tiles than compute units but fewer than twice as
+    many runs as two row slices in one launch, the first at split 2.  Rows
+    on both sides of the slice boundary, the ragged last tile and a random
+    sample match the oracle; repeated calls give the same bits; the unsliced
+    launch (forced split 1, or a workspace without room for the first
+    slice's words) matches the oracle too."""
+    rng = np.random.default_rng(stable_seed("row-slices", bits, batch, sparsity))
+    rows, cols = 64 * 300 + 17, 4096  # 301 tiles: 211 at split 2, then 90 whole (the last ragged)
+    boundary = 211 * 64
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, sparsity)
+    if sparsity == "none":
+        rp = col = val = None
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    sel = np.unique(np.concatenate([[0, 63, 64, boundary - 65, boundary - 64, boundary - 1, boundary, boundary + 1,
+                                     boundary + 63, boundary + 64, rows - 17, rows - 1],
+                                    rng.choice(rows, 1500, replace=False)]))
+    y_ref, scale = oracle.dense_sparse_gemv(codes[sel], lut, bits, rp, col, val, x, rows=rows, sel=sel)
+    sel_dev = torch.from_numpy(sel).cuda()
+    step(f"row slices bits={bits} batch={batch} {sparsity}")
+    y1 = d.fused()
+    y2 = d.fused()
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_u16(y1), dev_to_u16(y2)), "repeated sliced calls differ"
+    assert_close(y1[:, sel_dev], y_ref, scale, TOL, "sliced")
+    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    y3 = d.fused(ws=small)
+    try:
+        nw().set_tuning(split=1)
+        y4 = d.fused()
+        torch.cuda.synchronize()
+    finally:
+        nw().set_tuning()
+    assert_close(y3[:, sel_dev], y_ref, scale, TOL, "unsliced (small workspace)")
+    assert_close(y4[:, sel_dev], y_ref, scale, TOL, "unsliced (forced split 1)")
+    if sparsity != "none":
+        yd = d.gemv()
+        torch.cuda.synchronize()
+        yd_ref, dscale = oracle.dense_sparse_gemv(codes[sel], lut, bits, None, None, None, x, rows=rows, sel=sel)
+        assert_close(yd[:, sel_dev], yd_ref, dscale, TOL, "sliced dense-only")
+
+
 @pytest.mark.parametrize("batch", [4, 6, 8])
 def test_group_shared_x(batch):
     """Products that share one x (as q, k and v do) share one transposed copy
