@@ -85,9 +85,11 @@
  * again when the call's work on the stream is done.  When a call does not split (small shapes) the workspace may be
  * NULL, or smaller than sqllm_workspace_bytes() but at least the words: the
  * outliers then read x in place.  Results are bit-identical run to run whenever a row's columns
- * are split over at most two workgroups (all shapes up to 22016 x 22016 with
- * the built-in launch shapes); beyond that the fp32 partial sums are added
- * in arrival order.
+ * are split over at most two workgroups.  With the built-in launch shapes
+ * that holds for every product of more than 5440 rows (85 row tiles) or at
+ * most 5888 columns; a group launch counts the row tiles of all its
+ * products.  Below that (e.g. 64 x 22016: split 10) the fp32 partial sums
+ * are added in arrival order.
  */
 #ifndef SQLLM_H
 #define SQLLM_H

@@ -77,7 +77,8 @@ def test_pack_rejects_out_of_range_code():
 
 # ------------------------------------------------------------ products, small shapes
 
-SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8), (300, 4096, 1), (129, 1024, 16)]
+SHAPES = [(1, 256, 1), (7, 768, 3), (65, 512, 2), (130, 2048, 1), (257, 1024, 8), (300, 4096, 1), (129, 1024, 16),
+          (64, 22016, 2)]
 SPARSITY = ["none", "one", "5pct", "50pct", "full", "empty_rows", "dense_row"]
 
 
