@@ -474,12 +474,68 @@ def config_table(args) -> None:
         out.append(res)
         del copies, argv, packed, lut, rp, col, val
         torch.cuda.empty_cache()
+    # the 13B layer as a decoder layer issues it: one group launch per (q,k,v), (o), (gate,up), (down),
+    # every layer-sized copy of the seven products read once per 200 launches
+    specs3 = synth.workload(3)
+    mats3 = []
+    for i, spec in enumerate(specs3):
+        m = synth.make_matrix(spec, seed=args.seed, workload=3, index=i)
+        mats3.append(dict(
+            spec=spec, nnz=int(m.col.size), packed=nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits),
+            lut=torch.from_numpy(m.lut.view(np.int16)).cuda(), rp=torch.from_numpy(m.row_ptr).cuda(),
+            col=torch.from_numpy(m.col.view(np.int16)).cuda(), val=torch.from_numpy(m.val.view(np.int16)).cuda(),
+            x=torch.from_numpy(m.x.view(np.int16)).cuda(),
+            y=torch.empty(spec.rows, dtype=torch.int16, device="cuda")))
+    layer_bytes = sum(nw.algorithmic_bytes(d["spec"].rows, d["spec"].cols, d["spec"].bits, d["nnz"], 1) for d in mats3)
+    reps = max(1, -(-1024 * 2 ** 20 // layer_bytes))
+    layers = [mats3] + [[dict(d, **{k: d[k].clone() for k in ("packed", "lut", "rp", "col", "val")}) for d in mats3]
+                        for _ in range(reps - 1)]
+    levels = WeightStream.LEVELS
+    descs = []
+    for ms in layers:
+        for lv in levels:
+            arr = (nw.Product * len(lv))()
+            for k, i in enumerate(lv):
+                d = ms[i]
+                arr[k] = nw.Product(d["packed"].data_ptr(), d["lut"].data_ptr(), d["rp"].data_ptr(), d["col"].data_ptr(),
+                                    d["val"].data_ptr(), d["nnz"], d["spec"].rows, d["spec"].cols, d["x"].data_ptr(),
+                                    d["y"].data_ptr())
+            descs.append((arr, len(lv)))
+    gws = torch.zeros(max(int(nw.library().sqllm_group_workspace_bytes(a, n, 1)) for a, n in descs), dtype=torch.uint8,
+                      device="cuda")
+    gfn = nw.library().sqllm_dense_sparse_gemv_group
+    n_layers = 50
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for k in range(n_layers * len(levels)):
+            arr, n = descs[k % len(descs)]
+            st = gfn(arr, n, 3, 1, vp(gws.data_ptr()), gws.numel(), h)
+            if st != 0:
+                raise RuntimeError(f"sqllm_dense_sparse_gemv_group failed with status {st}")
+    ts = []
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n_layers)
+    layer_us = statistics.median(ts)
+    log(f"config 13B layer as four group launches: {layer_us:.2f} us, {layer_bytes / (layer_us * 1e3):.1f} GB/s")
+    del g, layers, descs, mats3
+    torch.cuda.empty_cache()
+
     totals = {}
     for wl, name in ((2, "mlp_pair"), (3, "layer")):
         sel = [r for r in out if r["workload"] == wl]
         us = sum(r["graph_us"] for r in sel)
         totals[f"workload{wl}_{name}"] = {"graph_us": round(us, 3), "GB_per_s": round(
             sum(r["bytes"] for r in sel) / (us * 1e3), 1)}
+    totals["workload3_layer_group_launches"] = {"graph_us": round(layer_us, 3),
+                                                "GB_per_s": round(layer_bytes / (layer_us * 1e3), 1)}
     print(json.dumps({"ablation": "configs", "unit": "us per product (median of 5 trials of 200 calls)",
                       "products": out, "totals": totals}), flush=True)
 
