@@ -309,6 +309,20 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
  *   SQLLM_ERR_SHAPE.  Results agree within the stated tolerance for every
  *   shape; not thread-safe against concurrent calls. */
 sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves, int sparse_naive, int dot_only);
+/*   sqllm_test_launch_plan: the launch the hot calls would make, without
+ *   making it (no device is touched; stand-in addresses are never read):
+ *   mode 0 = sqllm_dense_sparse_gemv (n = 1), 1 = sqllm_dense_sparse_gemv_group
+ *   with a separate x per product, 2 = the group with one x shared by all
+ *   products (equal cols).  rows / cols / nnz: HOST arrays of n; workspace_bytes
+ *   as the call would get it (0: no workspace).  plan: HOST array of 5 n + 1
+ *   ints; for product i, plan[5 i ..] = split (workgroups per row tile), column
+ *   groups per workgroup, waves per workgroup of its launch, 1 if its
+ *   outliers read a transposed copy of x, and for a single call run as two
+ *   row slices the row tiles of the first slice (which runs at the split
+ *   given; the rest runs whole), else 0; plan[5 n] = 1 for the matrix-core
+ *   form.  Argument and workspace errors as the calls report them. */
+sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const int64_t *cols, const int64_t *nnz,
+                                    int batch, size_t workspace_bytes, int *plan);
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
                                uint16_t *w, hipStream_t stream);
 

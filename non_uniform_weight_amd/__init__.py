@@ -70,13 +70,17 @@ _lib.sqllm_test_unpack.restype = _i32
 _lib.sqllm_test_unpack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
 _lib.sqllm_test_tuning.restype = _i32
 _lib.sqllm_test_tuning.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.sqllm_test_launch_plan.restype = _i32
+_lib.sqllm_test_launch_plan.argtypes = [_i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                        _i32, _sz, ctypes.POINTER(_i32)]
 _lib.sqllm_test_decode.restype = _i32
 _lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
 
 EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes", "sqllm_pack", "sqllm_gemv",
            "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_group_workspace_bytes",
            "sqllm_dense_sparse_gemv_group", "sqllm_quantize_workspace_bytes", "sqllm_outlier_thresholds",
-           "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning")
+           "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning",
+           "sqllm_test_launch_plan")
 MAX_GROUP = 8
 
 SQLLM_OK = 0
@@ -330,6 +334,20 @@ def set_tuning(target_wgs: int = 0, min_gps: int = 0, split: int = 0, waves: int
     (ablations)."""
     _check(_lib.sqllm_test_tuning(target_wgs, min_gps, split, waves, sparse_naive, dot_only),
            "sqllm_test_tuning")
+
+
+def launch_plan(shapes, batch: int = 1, workspace_bytes: int = 1 << 30, mode: int = 0):
+    """Test-only: the launch the calls would make for products of (rows, cols, nnz) in `shapes`, without a
+    device.  mode 0: one sqllm_dense_sparse_gemv; 1: one group call, a separate x per product; 2: one
+    group call, one shared x.  Per product: dict(split, gps, waves, xt, slice_tiles); plus the form."""
+    n = len(shapes)
+    arr = lambda k: (_i64 * n)(*[int(sh[k]) for sh in shapes])
+    out = (_i32 * (5 * n + 1))()
+    _check(_lib.sqllm_test_launch_plan(mode, n, arr(0), arr(1), arr(2), batch, workspace_bytes, out),
+           "sqllm_test_launch_plan")
+    items = [dict(split=out[5 * i], gps=out[5 * i + 1], waves=out[5 * i + 2], xt=out[5 * i + 3],
+                  slice_tiles=out[5 * i + 4]) for i in range(n)]
+    return items, ("matrix" if out[5 * n] else "dot")
 
 
 def algorithmic_bytes(rows: int, cols: int, bits: int, nnz: int, batch: int) -> int:

@@ -296,6 +296,84 @@ KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y,
     return a;
 }
 
+// Everything the single call decides before launching: the launch shape,
+// the transposed x, and the row slices of a product of 257..511 tiles.
+sqllm_status plan_single(KernelArgs &a, int bits, int batch, int64_t nnz, void *ws, size_t ws_bytes, LaunchShape &ls,
+                         XtJobs &jobs, GroupArgs &g, bool &sliced)
+{
+    choose_dense(a, batch, nnz, ls);
+    sqllm_status st = workspace_checks(a.split, a.rows, batch, ws, ws_bytes);
+    if (st != SQLLM_OK) return st;
+    plan_xt(a, batch, nnz, nnz, ws, ws_bytes, jobs);
+    sliced = slice_for_two_slots(a, bits, batch, ws, ws_bytes, g);
+    if (sliced) ls.waves = choose_waves((int64_t)g.item[0].tiles * g.item[0].split + g.item[1].tiles, g.item[0].gps);
+    return SQLLM_OK;
+}
+
+// One launch of a group call: the products with outliers (fused) or those
+// without.  g.n = 0 when there are none; which[k] is the item index of
+// g.item[k].
+sqllm_status plan_group_pass(const sqllm_product *items, int n, int batch, bool fused, void *workspace,
+                             size_t workspace_bytes, GroupArgs &g, LaunchShape &ls, XtJobs &jobs, int *which)
+{
+    g = GroupArgs{};
+    ls = LaunchShape{};
+    jobs = XtJobs{};
+    int64_t total_tiles = 0;
+    for (int i = 0; i < n; ++i)
+        if ((items[i].nnz > 0) == fused) total_tiles += tiles_of(items[i].rows);
+    if (total_tiles == 0) return SQLLM_OK;
+    size_t ws_off = 0;
+    int64_t wgs = 0;
+    void *own_ws[kMaxGroup];   // each product's workspace region (slots, then transposed x) or null
+    size_t own_bytes[kMaxGroup];
+    int64_t own_nnz[kMaxGroup];
+    for (int i = 0; i < n; ++i) {
+        const sqllm_product &p = items[i];
+        const size_t need = workspace_need(p.rows, p.cols, batch); // every product has its own region
+        if ((p.nnz > 0) != fused) {
+            ws_off += need;
+            continue;
+        }
+        void *mine = workspace ? (void *)((char *)workspace + ws_off) : nullptr;
+        const size_t left = workspace && workspace_bytes > ws_off ? workspace_bytes - ws_off : 0;
+        KernelArgs a = base_args(p.rows, p.cols, p.x, p.y, mine);
+        ws_off += need;
+        a.packed = p.packed;
+        a.lut = p.lut;
+        a.row_ptr = p.row_ptr;
+        a.col = p.col_idx;
+        a.val = p.val;
+        choose_split(a, total_tiles);
+        if (a.split > 1 && (!workspace || left < slots_need(p.rows, batch))) return SQLLM_ERR_WORKSPACE;
+        own_ws[g.n] = mine;
+        own_bytes[g.n] = left < need ? left : need;
+        own_nnz[g.n] = p.nnz;
+        which[g.n] = i;
+        g.item[g.n] = a;
+        if ((int64_t)a.tiles * a.split > g.wgs) g.wgs = a.tiles * a.split;
+        wgs += (int64_t)a.tiles * a.split;
+        ++g.n;
+    }
+    if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
+    wgs = fill_two_slots(g, wgs, own_ws, own_bytes, batch);
+    ls.mf = use_mf(batch);
+    int max_gps = 1;
+    for (int k = 0; k < g.n; ++k)
+        if (g.item[k].gps > max_gps) max_gps = g.item[k].gps;
+    ls.waves = choose_waves(wgs, max_gps);
+    // products that share x (as q, k and v do) share one transposed copy
+    for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);
+    for (int k = 0; k < g.n; ++k) {
+        int64_t nnz_x = 0; // nonzeros of this launch's products that gather from the same x
+        for (int j = 0; j < g.n; ++j)
+            if (g.item[j].x == g.item[k].x && g.item[j].cols == g.item[k].cols && !g.item[j].x_lds)
+                nnz_x += own_nnz[j];
+        plan_xt(g.item[k], batch, fused ? 1 : 0, nnz_x, own_ws[k], own_bytes[k], jobs);
+    }
+    return SQLLM_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -376,15 +454,12 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
     a.col = col_idx;
     a.val = val;
     LaunchShape ls{};
-    choose_dense(a, batch, nnz, ls);
-    st = workspace_checks(a.split, rows, batch, workspace, workspace_bytes);
-    if (st != SQLLM_OK) return st;
     XtJobs jobs{};
-    plan_xt(a, batch, nnz, nnz, workspace, workspace_bytes, jobs);
-    const Mode mode = nnz > 0 ? kFused : kDenseOnly;
     GroupArgs g;
-    const bool sliced = slice_for_two_slots(a, bits, batch, workspace, workspace_bytes, g);
-    if (sliced) ls.waves = choose_waves((int64_t)g.item[0].tiles * g.item[0].split + g.item[1].tiles, g.item[0].gps);
+    bool sliced = false;
+    st = plan_single(a, bits, batch, nnz, workspace, workspace_bytes, ls, jobs, g, sliced);
+    if (st != SQLLM_OK) return st;
+    const Mode mode = nnz > 0 ? kFused : kDenseOnly;
     if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
         (sliced ? launch_dense_sparse_group(g, bits, batch, mode, ls, stream)
                 : launch_dense_sparse(a, bits, batch, mode, ls, stream)) != hipSuccess ||
@@ -452,59 +527,13 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
     // products with outliers run in one launch, those without in another
     for (int pass = 0; pass < 2; ++pass) {
         const bool fused = pass == 0;
-        GroupArgs g{};
-        int64_t total_tiles = 0;
-        for (int i = 0; i < n; ++i)
-            if ((items[i].nnz > 0) == fused) total_tiles += tiles_of(items[i].rows);
-        if (total_tiles == 0) continue;
-        size_t ws_off = 0;
-        int64_t wgs = 0;
-        void *own_ws[kMaxGroup];   // each product's workspace region (slots, then transposed x) or null
-        size_t own_bytes[kMaxGroup];
-        int64_t own_nnz[kMaxGroup];
-        for (int i = 0; i < n; ++i) {
-            const sqllm_product &p = items[i];
-            const size_t need = workspace_need(p.rows, p.cols, batch); // every product has its own region
-            if ((p.nnz > 0) != fused) {
-                ws_off += need;
-                continue;
-            }
-            void *mine = workspace ? (void *)((char *)workspace + ws_off) : nullptr;
-            const size_t left = workspace && workspace_bytes > ws_off ? workspace_bytes - ws_off : 0;
-            KernelArgs a = base_args(p.rows, p.cols, p.x, p.y, mine);
-            ws_off += need;
-            a.packed = p.packed;
-            a.lut = p.lut;
-            a.row_ptr = p.row_ptr;
-            a.col = p.col_idx;
-            a.val = p.val;
-            choose_split(a, total_tiles);
-            if (a.split > 1 && (!workspace || left < slots_need(p.rows, batch))) return SQLLM_ERR_WORKSPACE;
-            own_ws[g.n] = mine;
-            own_bytes[g.n] = left < need ? left : need;
-            own_nnz[g.n] = p.nnz;
-            g.item[g.n] = a;
-            if ((int64_t)a.tiles * a.split > g.wgs) g.wgs = a.tiles * a.split;
-            wgs += (int64_t)a.tiles * a.split;
-            ++g.n;
-        }
-        if (wgs > INT32_MAX) return SQLLM_ERR_SHAPE;
-        wgs = fill_two_slots(g, wgs, own_ws, own_bytes, batch);
-        LaunchShape ls{};
-        ls.mf = use_mf(batch);
-        int max_gps = 1;
-        for (int k = 0; k < g.n; ++k)
-            if (g.item[k].gps > max_gps) max_gps = g.item[k].gps;
-        ls.waves = choose_waves(wgs, max_gps);
-        XtJobs jobs{}; // products that share x (as q, k and v do) share one transposed copy
-        for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);
-        for (int k = 0; k < g.n; ++k) {
-            int64_t nnz_x = 0; // nonzeros of this launch's products that gather from the same x
-            for (int j = 0; j < g.n; ++j)
-                if (g.item[j].x == g.item[k].x && g.item[j].cols == g.item[k].cols && !g.item[j].x_lds)
-                    nnz_x += own_nnz[j];
-            plan_xt(g.item[k], batch, fused ? 1 : 0, nnz_x, own_ws[k], own_bytes[k], jobs);
-        }
+        GroupArgs g;
+        LaunchShape ls;
+        XtJobs jobs;
+        int which[kMaxGroup];
+        sqllm_status st = plan_group_pass(items, n, batch, fused, workspace, workspace_bytes, g, ls, jobs, which);
+        if (st != SQLLM_OK) return st;
+        if (g.n == 0) continue;
         if (launch_xt_write(jobs, batch, stream) != hipSuccess ||
             launch_dense_sparse_group(g, bits, batch, fused ? kFused : kDenseOnly, ls, stream) != hipSuccess ||
             launch_xt_clear(jobs, batch, stream) != hipSuccess)
@@ -647,6 +676,81 @@ sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves
     t.force_waves = waves > 0 ? waves : dflt.force_waves;
     t.sparse_naive = sparse_naive;
     t.dot_only = dot_only;
+    return SQLLM_OK;
+}
+
+sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const int64_t *cols, const int64_t *nnz,
+                                    int batch, size_t workspace_bytes, int *plan)
+{
+    if (!rows || !cols || !nnz || !plan) return SQLLM_ERR_NULL;
+    if (mode < 0 || mode > 2 || n < 1 || n > kMaxGroup || (mode == 0 && n != 1)) return SQLLM_ERR_SHAPE;
+    if (batch < 1 || batch > kMaxBatch) return SQLLM_ERR_BATCH;
+    for (int i = 0; i < n; ++i) {
+        const sqllm_status st = check_shape(rows[i], cols[i]);
+        if (st != SQLLM_OK) return st;
+        if (nnz[i] < 0 || nnz[i] >= ((int64_t)1 << 31)) return SQLLM_ERR_SHAPE;
+        if (mode == 2 && cols[i] != cols[0]) return SQLLM_ERR_SHAPE;
+    }
+    // stand-ins for device addresses: aligned, distinct, never dereferenced (nothing is launched)
+    const uintptr_t base = (uintptr_t)1 << 40, stride = (uintptr_t)1 << 36;
+    auto fake = [&](int i, int k) { return (void *)(base + (uintptr_t)(i * 8 + k) * stride); };
+    void *ws = workspace_bytes ? (void *)(base / 2) : nullptr;
+    if (mode == 0) {
+        KernelArgs a = base_args(rows[0], cols[0], (const uint16_t *)fake(0, 0), (uint16_t *)fake(0, 1), ws);
+        a.packed = fake(0, 2);
+        a.lut = (const uint16_t *)fake(0, 3);
+        if (nnz[0] > 0) {
+            a.row_ptr = (const int32_t *)fake(0, 4);
+            a.col = (const uint16_t *)fake(0, 5);
+            a.val = (const uint16_t *)fake(0, 6);
+        }
+        LaunchShape ls{};
+        XtJobs jobs{};
+        GroupArgs g;
+        bool sliced = false;
+        const sqllm_status st = plan_single(a, 3, batch, nnz[0], ws, workspace_bytes, ls, jobs, g, sliced);
+        if (st != SQLLM_OK) return st;
+        plan[0] = sliced ? g.item[0].split : a.split;
+        plan[1] = sliced ? g.item[0].gps : a.gps;
+        plan[2] = ls.waves;
+        plan[3] = a.xt ? 1 : 0;
+        plan[4] = sliced ? g.item[0].tiles : 0;
+        plan[5] = ls.mf;
+        return SQLLM_OK;
+    }
+    sqllm_product items[kMaxGroup];
+    for (int i = 0; i < n; ++i) {
+        sqllm_product &p = items[i];
+        p.packed = fake(i, 2);
+        p.lut = (const uint16_t *)fake(i, 3);
+        p.row_ptr = nnz[i] > 0 ? (const int32_t *)fake(i, 4) : nullptr;
+        p.col_idx = nnz[i] > 0 ? (const uint16_t *)fake(i, 5) : nullptr;
+        p.val = nnz[i] > 0 ? (const uint16_t *)fake(i, 6) : nullptr;
+        p.nnz = nnz[i];
+        p.rows = rows[i];
+        p.cols = cols[i];
+        p.x = (const uint16_t *)fake(mode == 2 ? 0 : i, 0);
+        p.y = (uint16_t *)fake(i, 1);
+    }
+    int mf = use_mf(batch);
+    for (int pass = 0; pass < 2; ++pass) {
+        GroupArgs g;
+        LaunchShape ls;
+        XtJobs jobs;
+        int which[kMaxGroup];
+        const sqllm_status st = plan_group_pass(items, n, batch, pass == 0, ws, workspace_bytes, g, ls, jobs, which);
+        if (st != SQLLM_OK) return st;
+        for (int k = 0; k < g.n; ++k) {
+            int *q = plan + 5 * which[k];
+            q[0] = g.item[k].split;
+            q[1] = g.item[k].gps;
+            q[2] = ls.waves;
+            q[3] = g.item[k].xt ? 1 : 0;
+            q[4] = 0;
+        }
+        if (g.n) mf = ls.mf;
+    }
+    plan[5 * n] = mf;
     return SQLLM_OK;
 }
 

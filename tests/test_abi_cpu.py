@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
@@ -269,3 +269,99 @@ def test_bytes_accounting_2bit_against_appendix_f(nwpkg):
     stored = sum(nwpkg.algorithmic_bytes(r, c, 2, 0, 1) - 2 * c - 2 * r for r, c in LLAMA2_13B)
     avg = 8 * stored / weights
     assert int(avg * 100) / 100 == 2.01
+
+
+# ---------------------------------------------------------------- launch planning (host logic, no device)
+
+P65 = [(8192, 8192, 301990), (22016, 8192, 811598), (8192, 22016, 811598)]
+
+
+@pytest.mark.parametrize("shape,split,gps,waves,slice_tiles", [
+    ((8192, 8192, 301990), 2, 16, 8, 0),      # 128 tiles: one workgroup per unit, two groups per wave
+    ((22016, 8192, 811598), 2, 16, 8, 168),   # 344 tiles: 168 at split 2 + 176 whole = 512 workgroups
+    ((8192, 22016, 811598), 2, 43, 16, 0),    # 43 groups per workgroup: 16 waves
+    ((4096, 4096, 75497), 2, 8, 8, 0),        # at least 8 groups per workgroup caps the split
+    ((11008, 4096, 202899), 1, 16, 8, 0),     # 172 tiles: split rounded down (344 workgroups measured slower)
+    ((13824, 5120, 318505), 1, 20, 12, 0),    # 20 groups per workgroup: 12 waves
+    ((5120, 13824, 318505), 3, 18, 12, 0),    # 80 tiles: floor(256 / 80) = 3
+    ((64, 22016, 6000), 10, 9, 8, 0),         # one tile: split up to the 8-group floor
+    ((150 * 64, 4096, 1000), 2, 8, 8, 0),     # 150 tiles would leave 41% of the units idle: one split more
+])
+def test_single_call_launch_rules(nwpkg, shape, split, gps, waves, slice_tiles):
+    (plan,), form = nwpkg.launch_plan([shape])
+    assert (plan["split"], plan["gps"], plan["waves"], plan["slice_tiles"]) == (split, gps, waves, slice_tiles)
+    assert form == "matrix"
+
+
+def test_row_slices_need_the_workspace_words(nwpkg):
+    """Without room for the first slice's words the product runs whole at split 1."""
+    (plan,), _ = nwpkg.launch_plan([P65[1]], workspace_bytes=0)
+    assert (plan["split"], plan["slice_tiles"]) == (1, 0)
+    words = 168 * 64 * 8  # (fp32 sum, count) per row of the 168 tiles, batch 1
+    (plan,), _ = nwpkg.launch_plan([P65[1]], workspace_bytes=words)
+    assert plan["slice_tiles"] == 168
+    (plan,), _ = nwpkg.launch_plan([P65[1]], workspace_bytes=words - 8)
+    assert plan["slice_tiles"] == 0
+
+
+def test_group_launch_rules(nwpkg):
+    # (q, k, v): 384 tiles; q at split 2 fills one slot of every unit, k and v the other
+    plans, _ = nwpkg.launch_plan([P65[0]] * 3, mode=2)
+    assert [(p["split"], p["gps"], p["waves"]) for p in plans] == [(2, 16, 8), (1, 32, 8), (1, 32, 8)]
+    # (gate, up): 688 tiles, whole tiles (every mix of half tiles measured slower)
+    plans, _ = nwpkg.launch_plan([P65[1]] * 2, mode=2)
+    assert [(p["split"], p["waves"]) for p in plans] == [(1, 8), (1, 8)]
+    # (o) and (down) alone
+    assert nwpkg.launch_plan([P65[0]], mode=1)[0][0]["split"] == 2
+    assert [nwpkg.launch_plan([P65[2]], mode=1)[0][0][k] for k in ("split", "gps", "waves")] == [2, 43, 16]
+    # products without outliers go to a launch of their own, planned from their own tiles
+    plans, _ = nwpkg.launch_plan([P65[0], (8192, 8192, 0)], mode=1)
+    assert [p["split"] for p in plans] == [2, 2]
+
+
+def test_transposed_x_rule(nwpkg):
+    """From batch 5, outliers gather from a transposed x when the products reading that x carry at least
+    400K nonzeros and the workspace holds it."""
+    assert nwpkg.launch_plan([P65[0]] * 3, batch=8, mode=2)[0][0]["xt"] == 1      # 906K nonzeros share one x
+    assert nwpkg.launch_plan([P65[0]] * 3, batch=8, mode=1)[0][0]["xt"] == 0      # 302K each
+    assert nwpkg.launch_plan([P65[0]] * 3, batch=4, mode=2)[0][0]["xt"] == 0      # below batch 5
+    assert nwpkg.launch_plan([P65[1]], batch=6)[0][0]["xt"] == 1
+    small = nwpkg.workspace_bytes(22016, 8192, 6) - 1
+    assert nwpkg.launch_plan([P65[1]], batch=6, workspace_bytes=small)[0][0]["xt"] == 0
+
+
+def test_dense_form_rule(nwpkg):
+    try:
+        nwpkg.set_tuning(dot_only=1)
+        assert nwpkg.launch_plan([P65[0]], batch=8)[1] == "dot"
+        assert nwpkg.launch_plan([P65[0]], batch=9)[1] == "matrix"   # no dot form above batch 8
+    finally:
+        nwpkg.set_tuning()
+    assert nwpkg.launch_plan([P65[0]], batch=1)[1] == "matrix"
+
+
+def test_forced_shapes_turn_the_rules_off(nwpkg):
+    try:
+        nwpkg.set_tuning(split=1)
+        (plan,), _ = nwpkg.launch_plan([P65[1]])
+        assert (plan["split"], plan["slice_tiles"]) == (1, 0)
+        plans, _ = nwpkg.launch_plan([P65[0]] * 3, mode=2)
+        assert [p["split"] for p in plans] == [1, 1, 1]
+    finally:
+        nwpkg.set_tuning()
+
+
+def test_launch_plan_argument_errors(lib):
+    one = (ctypes.c_int64 * 1)(64)
+    cols = (ctypes.c_int64 * 1)(256)
+    nnz = (ctypes.c_int64 * 1)(0)
+    out = (ctypes.c_int * 6)()
+    f = lib.sqllm_test_launch_plan
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    assert f(0, 1, one, cols, nnz, 1, 0, out) == 0
+    assert f(0, 2, one, cols, nnz, 1, 0, out) != 0        # a single call plans one product
+    assert f(3, 1, one, cols, nnz, 1, 0, out) != 0
+    assert f(0, 1, one, cols, nnz, 17, 0, out) != 0
+    assert f(0, 1, one, (ctypes.c_int64 * 1)(300), nnz, 1, 0, out) != 0   # cols not a multiple of 256
+    assert f(0, 1, None, cols, nnz, 1, 0, out) != 0
