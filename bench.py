@@ -705,7 +705,7 @@ def main():
         log(f"cpu baseline: {cpu['value']} GB/s with {threads} threads")
 
     out = {
-        "metric": "effective HBM GB/s (% of peak) and \u00b5s/GEMV, 3-bit LUT+sparse, batch 1",
+        "metric": f"effective HBM GB/s (% of peak) and \u00b5s/GEMV, {args.bits}-bit LUT+sparse, batch 1",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
