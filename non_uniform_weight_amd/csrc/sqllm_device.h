@@ -535,10 +535,14 @@ __device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it,
     }
 }
 
-// Chunks of 64 nonzeros a wave loads per round: column | fp16 value << 16,
-// one register per chunk, held through the dense steps (fewer where the
-// ring is large, and above batch 8).
-constexpr int round_chunks(int bits, int batch) { return bits == 3 && batch == 1 ? 8 : (batch > 8 ? 2 : 4); }
+// Chunks of 64 nonzeros a wave loads per round (two registers per chunk:
+// column and value), the first round held through the dense steps.  Fewer
+// above batch 8, and at 2 bits and batch 1, where 4 made the matrix-core
+// group kernel spill 8 registers (2: the 2-bit stream 5% faster).
+constexpr int round_chunks(int bits, int batch)
+{
+    return bits == 3 && batch == 1 ? 8 : (batch > 8 || (bits == 2 && batch == 1) ? 2 : 4);
+}
 
 // Loads of nonzeros [base, base + 64 * R): column and raw fp16 value of one
 // nonzero per lane and chunk, each zero-extended in a register of its own (so
