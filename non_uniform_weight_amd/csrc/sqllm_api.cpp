@@ -185,13 +185,14 @@ bool slice_for_two_slots(const KernelArgs &a, int bits, int batch, void *ws, siz
 int use_mf(int batch) { return tuning().dot_only && batch <= kMaxDotBatch ? 0 : 1; }
 
 // Stage x in LDS for the outlier gathers when it fits beside the pair table
-// (in half of the LDS when two workgroups share a unit).
-void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int waves, LaunchShape &ls)
+// (in half of the LDS when the launch has more workgroups than units, so
+// that two share a unit).
+void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int64_t workgroups, LaunchShape &ls)
 {
     a.x_lds = 0;
     if (nnz <= 0) return;
     const size_t staged = staged_x_bytes(a.cols, batch);
-    const size_t budget = waves <= kDefaultWaves ? kLdsBudget / 2 : kLdsBudget;
+    const size_t budget = workgroups > tuning().target_wgs ? kLdsBudget / 2 : kLdsBudget;
     if (kTableBytes + staged <= budget) {
         a.x_lds = 1;
         if (staged > ls.dyn_lds) ls.dyn_lds = staged;
@@ -204,7 +205,7 @@ void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
     ls.mf = use_mf(batch);
     ls.waves = choose_waves((int64_t)a.tiles * a.split, a.gps);
     ls.dyn_lds = 0;
-    choose_x_lds(a, batch, nnz, ls.waves, ls);
+    choose_x_lds(a, batch, nnz, (int64_t)a.tiles * a.split, ls);
 }
 
 // Outlier-only kernel: about kSparseShare nonzeros per wave; x staged in LDS
@@ -363,7 +364,7 @@ sqllm_status plan_group_pass(const sqllm_product *items, int n, int batch, bool 
         if (g.item[k].gps > max_gps) max_gps = g.item[k].gps;
     ls.waves = choose_waves(wgs, max_gps);
     // products that share x (as q, k and v do) share one transposed copy
-    for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, ls.waves, ls);
+    for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, wgs, ls);
     for (int k = 0; k < g.n; ++k) {
         int64_t nnz_x = 0; // nonzeros of this launch's products that gather from the same x
         for (int j = 0; j < g.n; ++j)
