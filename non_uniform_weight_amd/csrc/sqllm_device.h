@@ -54,6 +54,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <utility>
 
 #include "sqllm_internal.h"
@@ -1029,18 +1030,31 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(Grou
     product_body<BITS, B, MODE, MF>(a, blockIdx.x);
 }
 
+// Ask once per kernel and device for more than the default dynamic LDS (the
+// attribute belongs to the device current at the call).  Not fatal when
+// refused: launches within the default limit still work, larger ones report
+// the launch error.
+inline void raise_lds_limit(const void *kern, std::atomic<uint64_t> &done, int bytes)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_relaxed) & bit) return;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+        (void)hipGetLastError();
+    done.fetch_or(bit, std::memory_order_relaxed);
+}
+
 template <int BITS, int B, int MODE, bool MF>
 hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
     auto kern = dense_sparse_kernel<BITS, B, MODE, MF>;
-    static bool attr_set = false; // ask once for more than the default dynamic LDS
-    if (!attr_set) {
-        const int static_lds = MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4;
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsBudget - static_lds) != hipSuccess)
-            (void)hipGetLastError(); // not fatal: launches within the default limit still work
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_devices{0};
+    raise_lds_limit((const void *)kern, attr_devices,
+                    kLdsBudget - (MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4));
     if (ls.waves < 1 || ls.waves > kMaxWaves) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(a.tiles * a.split)), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, a);
@@ -1051,13 +1065,8 @@ template <int BITS, int B, int MODE, bool MF>
 hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
     auto kern = dense_sparse_group_kernel<BITS, B, MODE, MF>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsBudget - kTableBytes) != hipSuccess)
-            (void)hipGetLastError();
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_devices{0};
+    raise_lds_limit((const void *)kern, attr_devices, kLdsBudget - kTableBytes);
     if (ls.waves < 1 || ls.waves > kMaxWaves || g.n < 1 || g.n > kMaxGroup) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)g.wgs, (unsigned)g.n), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, g);
