@@ -617,6 +617,10 @@ def offline_ablation(args) -> None:
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the design notes describe row sharding across GPUs).", file=sys.stderr)
+        sys.exit(2)
     if args.ablation == "outliers":
         outlier_ablation(args)
         return
@@ -629,10 +633,6 @@ def main():
     if args.ablation == "configs":
         config_table(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the design notes describe row sharding across GPUs).", file=sys.stderr)
-        sys.exit(2)
     import torch
 
     import synth
