@@ -78,9 +78,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (one per compute unit; a few more leave a tail in which some units run two
 // workgroups: 11008x4096 at split 2, 344 workgroups, measured 10.8 us against
 // 8.3 at split 1), one split more only when fewer than 60% of the units would
-// be busy, and at least min_gps groups per workgroup.  With
-// outliers x is staged in LDS when it fits beside the pair table -- for two
-// workgroups per compute unit when there are more workgroups than units.
+// be busy, and at least min_gps groups per workgroup.
 // total_tiles: row tiles of every product sharing the launch.
 void choose_split(KernelArgs &a, int64_t total_tiles)
 {

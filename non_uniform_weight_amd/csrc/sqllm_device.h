@@ -31,10 +31,12 @@
 //   outlier chunks: the tile's CSR nonzeros are cut into even shares, one per
 //   wave of the split (balanced whatever the per-row skew: §3.4 "Kernel
 //   Implementation", balanced sparse kernel; Appendix C), 64 per lane-wide
-//   chunk.  Within a chunk the rows are non-decreasing: each row that starts
-//   there marks its first lane, a ballot of the marks gives every lane its
-//   segment start, x is gathered, and a DPP segmented scan sums each row's
-//   products; the row's own lane fetches its sum.  When all of x is staged
+//   chunk.  Within a chunk the rows are non-decreasing: x is gathered, one
+//   inclusive prefix sum of the products runs over the wave (DPP row shifts
+//   and row broadcasts), and a row's sum is the prefix at its last lane in
+//   the chunk less the prefix at the lane before its first, which the row's
+//   own lane fetches with two lane permutes (no search for segment starts,
+//   no atomics).  When all of x is staged
 //   in LDS a chunk follows each dense group; otherwise the chunks come after
 //   the dense groups, a round at a time (all of a round's gathers, then its
 //   scans), reading x through the cache or, from batch 5 on, from a
@@ -691,7 +693,8 @@ __device__ __forceinline__ void sparse_chunk(uint32_t colv, uint32_t valv, int c
 constexpr bool kRingAfterTable = true;
 
 // Quads (16 bytes) of x each thread stages in LDS from registers loaded in
-// the prologue; wider x is copied after the ring is issued.
+// the prologue; the rest of a wider x is copied in a loop before the table
+// barrier.
 constexpr int kStageQuads = 4;
 
 // Round and store (or hand over) this workgroup's fp32 row sums.
