@@ -479,6 +479,62 @@ def test_group_matches_oracle(bits, batch):
         assert_close(y, y_ref, scale, TOL, f"group item {shape}")
 
 
+def test_group_graph_replay_matches_eager():
+    """Group launches captured in a HIP graph give, on every replay, the bits
+    of the same launches made eagerly: a layer's (q, k, v) (two workgroups per
+    unit, q at split 2) and (gate, up) at batch 1, and a batch-6 group whose
+    products share one x (its transposed copy is written and cleared by
+    kernels inside the graph).  Eager calls run between the replays."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    specs = synth.workload(5, bits=3, density_bp=45)[:7]
+    groups = []
+    for level in ([0, 1, 2], [4, 5]):
+        ms = [synth.make_matrix(specs[i], seed=5, workload=5, index=i) for i in level]
+        groups.append(([DevMatrix.from_synth(m) for m in ms], 1))
+    rng = np.random.default_rng(stable_seed("group-graph"))
+    x6 = (rng.standard_normal((6, 4096))).astype(np.float16).view(np.uint16)
+    mats6 = []
+    for k in range(3):
+        codes, lut, _, rp, col, val = _make_case(rng, 1024, 4096, 3, 6, "50pct")
+        d = DevMatrix(codes, lut, 3, rp, col, val, x6)
+        mats6.append(d)
+    shared = mats6[0].x
+    for d in mats6:
+        d.x = shared
+    groups.append((mats6, 6))
+    step("group graph: eager")
+    eager = []
+    for mats, batch in groups:
+        ys = [torch.empty((batch, d.rows), dtype=torch.float16, device="cuda") for d in mats]
+        nw().dense_sparse_gemv_group(_items(mats, ys), 3, ws=ws)
+        eager.append(ys)
+    torch.cuda.synchronize()
+    eager = [[dev_to_u16(y) for y in ys] for ys in eager]
+    outs = [[torch.empty((batch, d.rows), dtype=torch.float16, device="cuda") for d in mats] for mats, batch in groups]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    step("group graph: capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for (mats, batch), ys in zip(groups, outs):
+                nw().dense_sparse_gemv_group(_items(mats, ys), 3, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        step(f"group graph replay {rep}")
+        for ys in outs:
+            for y in ys:
+                y.fill_(float("nan"))
+        mats6[1].fused(ws=ws)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for gi, (ys, refs) in enumerate(zip(outs, eager)):
+            for k, (y, ref) in enumerate(zip(ys, refs)):
+                assert np.array_equal(dev_to_u16(y), ref), f"replay {rep} group {gi} product {k} differs"
+    assert int(ws.view(torch.int32).abs().sum().item()) == 0, "workspace not zero after the replays"
+
+
 @pytest.mark.parametrize("split", [1, 2])
 def test_group_equals_single_calls(split):
     """With the launch shape fixed, a product computed inside a group has the
