@@ -479,6 +479,30 @@ def test_group_matches_oracle(bits, batch):
         assert_close(y, y_ref, scale, TOL, f"group item {shape}")
 
 
+@pytest.mark.parametrize("batch", [1, 5])
+def test_group_of_eight_products(batch):
+    """The most products a group call takes (8): with and without outliers
+    mixed (two launches), ragged shapes, distinct x; each matches the oracle."""
+    rng = np.random.default_rng(stable_seed("group-eight", batch))
+    shapes = [(193, 4096, "5pct"), (64, 256, "none"), (300, 2048, "none"), (1000, 1024, "empty_rows"),
+              (7, 768, "full"), (129, 512, "dense_row"), (65, 8192, "one"), (257, 1024, "none")]
+    cases = [_make_case(rng, r, c, 3, batch, sp) for r, c, sp in shapes]
+    mats = []
+    for (r, c, sp), (codes, lut, x, rp, col, val) in zip(shapes, cases):
+        if sp == "none":
+            rp = col = val = None
+        mats.append(DevMatrix(codes, lut, 3, rp, col, val, x))
+    ys = [torch.full((batch, d.rows), float("nan"), dtype=torch.float16, device="cuda") for d in mats]
+    step(f"group of eight batch {batch}")
+    nw().dense_sparse_gemv_group(_items(mats, ys), 3)
+    torch.cuda.synchronize()
+    for (r, c, sp), (codes, lut, x, rp, col, val), y in zip(shapes, cases, ys):
+        if sp == "none":
+            rp = col = val = None
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+        assert_close(y, y_ref, scale, TOL, f"group item {r}x{c} {sp}")
+
+
 def test_group_graph_replay_matches_eager():
     """Group launches captured in a HIP graph give, on every replay, the bits
     of the same launches made eagerly: a layer's (q, k, v) (two workgroups per
