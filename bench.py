@@ -230,9 +230,30 @@ def cpu_baseline(stream_specs, seed: int, threads: int, min_seconds: float = 10.
             elapsed += time.perf_counter() - t0
             total_bytes += nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, int(m.col.size), spec.batch)
         passes += 1
+    # the same oracle on one thread, over the layer's first linear once (a few seconds)
+    m = mats[0]
+    t0 = time.perf_counter()
+    oracle.dense_sparse_gemv(m.codes, m.lut, m.spec.bits, m.row_ptr if m.col.size else None, m.col, m.val, m.x,
+                             threads=1)
+    t1 = time.perf_counter() - t0
+    b1 = nw.algorithmic_bytes(m.spec.rows, m.spec.cols, m.spec.bits, int(m.col.size), m.spec.batch)
     return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of the stream: 7 linears, all rows, {passes} passes ({total_bytes / 1e6:.1f} MB "
-                      f"algorithmic), fp64 oracle incl. the |W||x| normaliser, {elapsed:.1f} s"}
+                      f"algorithmic), fp64 oracle incl. the |W||x| normaliser, {elapsed:.1f} s",
+            "cpu_model": _cpu_model(), "cpus_visible": os.cpu_count(),
+            "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{m.spec.rows}x{m.spec.cols} once, {t1:.1f} s"}}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def outlier_ablation(args) -> None:
