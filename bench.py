@@ -18,8 +18,8 @@ bits + fp16 tables + CSR at 4 B per nonzero + int32 row pointers + x + y)
 divided by the time per step; also microseconds per GEMV.  The pages' kernel
 ran on other hardware and prints no GB/s figure, so vs_baseline is null.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
-GPU (sharding by output rows is described in the design notes).
+Prints one JSON line.  ``--gpus`` above 1 is refused: the benchmark runs on
+one GPU (sharding by output rows is described in the design notes).
 """
 from __future__ import annotations
 
