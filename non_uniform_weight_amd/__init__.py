@@ -130,19 +130,27 @@ def workspace_bytes(rows: int, cols: int, batch: int) -> int:
 _WORKSPACES: dict = {}
 
 
-def workspace(rows: int, cols: int, batch: int, device=None) -> torch.Tensor:
-    """Zero-filled workspace cached per device (grown on demand).  Calls that
-    share it must be ordered on one stream."""
-    return _cached_workspace(workspace_bytes(rows, cols, batch), device)
+def workspace(rows: int, cols: int, batch: int, device=None, stream=None) -> torch.Tensor:
+    """Zero-filled workspace cached per (device, stream), grown on demand.
+    The calls leave it all zero again; calls on one stream are ordered, so
+    they may share it, and each stream gets its own."""
+    return _cached_workspace(workspace_bytes(rows, cols, batch), device, stream)
 
 
-def _cached_workspace(nbytes: int, device=None) -> torch.Tensor:
+def _cached_workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.index, s.cuda_stream)
     need = max(nbytes, 256)
-    ws = _WORKSPACES.get(device)
+    ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=device)
-        _WORKSPACES[device] = ws
+        # zeroed on the stream that will use it, so the fill is ordered before
+        # the call; a smaller buffer it replaces is freed to that same stream
+        with torch.cuda.stream(s):
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
     return ws
 
 
@@ -176,7 +184,7 @@ def gemv(packed, lut, bits, x, y=None, ws=None, stream=None) -> torch.Tensor:
     """y = D x (dense part)."""
     rows = lut.shape[0]
     x, y, batch, cols = _x_y(x, y, rows)
-    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    ws = workspace(rows, cols, batch, x.device, stream) if ws is None else ws
     _check(_lib.sqllm_gemv(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16), bits, rows, cols,
                            _dev(x, "x", torch.float16), batch, _dev(y, "y", torch.float16),
                            _dev(ws, "workspace", torch.uint8), ws.numel(), _stream(stream)), "sqllm_gemv")
@@ -196,7 +204,7 @@ def spmv_add(row_ptr, col, val, x, y, ws=None, stream=None) -> torch.Tensor:
     """y += S x in place (col: uint16, or int16 holding the same bits)."""
     rows = row_ptr.shape[0] - 1
     x, y, batch, cols = _x_y(x, y, rows)
-    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    ws = workspace(rows, cols, batch, x.device, stream) if ws is None else ws
     rp, ci, cv, nnz = _csr_ptrs(row_ptr, col, val)
     _check(_lib.sqllm_spmv_add(rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
                                _dev(y, "y", torch.float16), _dev(ws, "workspace", torch.uint8), ws.numel(),
@@ -208,7 +216,7 @@ def dense_sparse_gemv(packed, lut, bits, row_ptr, col, val, x, y=None, ws=None, 
     """y = (D + S) x in one launch."""
     rows = lut.shape[0]
     x, y, batch, cols = _x_y(x, y, rows)
-    ws = workspace(rows, cols, batch, x.device) if ws is None else ws
+    ws = workspace(rows, cols, batch, x.device, stream) if ws is None else ws
     rp, ci, cv, nnz = _csr_ptrs(row_ptr, col, val)
     _check(_lib.sqllm_dense_sparse_gemv(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16), bits,
                                         rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
@@ -247,7 +255,7 @@ def dense_sparse_gemv_group(items, bits: int, ws: torch.Tensor | None = None, st
     arr, batch = group_products(items, bits)
     need = int(_lib.sqllm_group_workspace_bytes(arr, len(items), batch))
     if ws is None:
-        ws = _cached_workspace(need, items[0]["x"].device)
+        ws = _cached_workspace(need, items[0]["x"].device, stream)
     _check(_lib.sqllm_dense_sparse_gemv_group(arr, len(items), bits, batch, _dev(ws, "workspace", torch.uint8),
                                               ws.numel(), _stream(stream)), "sqllm_dense_sparse_gemv_group")
 
