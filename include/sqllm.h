@@ -21,7 +21,9 @@
  *
  * Arithmetic: every product of two fp16 values is formed exactly and summed
  * in fp32; the fused call rounds each output once to fp16 (round to nearest
- * even).  Summation order is fixed, so repeated calls give identical bits.
+ * even).  For a given shape, batch and workspace size the launch shape is
+ * fixed and every sum is taken in a fixed order (including the combine of a
+ * row's column split, below), so repeated calls give identical bits.
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -70,26 +72,27 @@
  *   The packed buffer must be 16-byte aligned.
  *
  * Workspace: the hot calls may split a row's columns over several
- * workgroups, which then combine their fp32 partial sums on the device.
- * They take a caller-owned workspace of at least
+ * workgroups (at most 16), which then combine their fp32 partial sums on the
+ * device.  They take a caller-owned workspace of at least
  * sqllm_workspace_bytes(rows, cols, batch) bytes, 256-byte aligned,
- * ZERO-FILLED before its first use: one 8-byte (fp32 sum, count) word per
- * output, which the workgroup completing an output resets to zero.  Every
- * call therefore leaves it ready for the next one, so one workspace serves
- * any sequence of calls, of any shapes it is large enough for, that are
- * ordered on one stream.  Calls that may run concurrently need separate
- * workspaces.  At batch >= 5 the workspace also holds, behind the words, a
- * transposed copy of x ([cols][8] fp16, [cols][16] above batch 8) from which the outliers
- * read all batch columns of a column in one load; the call writes it before
- * its product kernel and clears it after, so the whole workspace is zero
- * again when the call's work on the stream is done.  When a call does not split (small shapes) the workspace may be
- * NULL, or smaller than sqllm_workspace_bytes() but at least the words: the
- * outliers then read x in place.  Results are bit-identical run to run whenever a row's columns
- * are split over at most two workgroups.  With the built-in launch shapes
- * that holds for every product of more than 5440 rows (85 row tiles) or at
- * most 5888 columns; a group launch counts the row tiles of all its
- * products.  Below that (e.g. 64 x 22016: split 10) the fp32 partial sums
- * are added in arrival order.
+ * ZERO-FILLED before its first use.  With the columns split over s > 1
+ * workgroups a call uses s - 1 eight-byte words per output: the partial sums
+ * meet in a binary tree (splits 2j and 2j+1 pair up, one atomic OR each sets
+ * its half of the pair's word, the second arrival adds left + right), so
+ * the order of the fp32 additions does not depend on which workgroup
+ * arrives first; every word is reset by the workgroup that completes it.
+ * Every call therefore leaves the workspace ready for the next one, so one
+ * workspace serves any sequence of calls, of any shapes it is large enough
+ * for, that are ordered on one stream.  Calls that may run concurrently
+ * need separate workspaces.  At batch >= 5 the workspace also holds, after
+ * the words of the largest split, a transposed copy of x ([cols][8] fp16,
+ * [cols][16] above batch 8) from which the outliers read all batch columns
+ * of a column in one load; the call writes it before its product kernel and
+ * clears it after, so the whole workspace is zero again when the call's work
+ * on the stream is done.  A call that does not split (small shapes) needs no
+ * words: the workspace may then be NULL, and a workspace with room for the
+ * words of the call's split but smaller than sqllm_workspace_bytes() makes
+ * the outliers read x in place.
  */
 #ifndef SQLLM_H
 #define SQLLM_H
@@ -124,10 +127,10 @@ const char *sqllm_status_string(sqllm_status s);
 size_t sqllm_packed_bytes(int64_t rows, int64_t cols, int bits);
 
 /* Bytes of workspace the hot calls need for this shape and batch (the same
- * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv):
- * ceil(rows / 64) * 64 * batch * 8, plus at batch >= 5 the transposed x,
- * cols * 16 (cols * 32 above batch 8) rounded up to 256; 0 if the arguments
- * are out of range. */
+ * bound covers sqllm_gemv, sqllm_spmv_add and sqllm_dense_sparse_gemv): the
+ * words of the largest split, ceil(rows / 64) * 64 * batch * 8 * 15, plus at
+ * batch >= 5 the transposed x, cols * 16 (cols * 32 above batch 8) rounded
+ * up to 256; 0 if the arguments are out of range. */
 size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch);
 
 /*
@@ -137,12 +140,16 @@ size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch);
  *   codes:  device uint8 [rows][cols], every value < 2^bits
  *   packed: device buffer of sqllm_packed_bytes(rows, cols, bits) bytes,
  *           16-byte aligned; padding rows are written as zeros
+ *   workspace: caller-owned device memory of at least 4 bytes, 4-byte
+ *           aligned, for the call's error flag; its first 4 bytes are zero
+ *           again when the call returns (so a hot-call workspace may serve);
+ *           the library allocates nothing
  * The code range is checked on the device; the call SYNCHRONISES `stream`
  * to report SQLLM_ERR_CODE_RANGE (packed contents are then unspecified).
- * It allocates (and frees) one 4-byte device flag.
+ * A missing or too small workspace is SQLLM_ERR_WORKSPACE.
  */
-sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed,
-                        hipStream_t stream);
+sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * sqllm_gemv -- dense part only: y = D x.
@@ -297,9 +304,9 @@ sqllm_status sqllm_test_unpack(const void *packed, int64_t rows, int64_t cols, i
                                hipStream_t stream);
 /*   sqllm_test_tuning: launch shape of later calls in this process: the
  *   workgroup count the column split aims for, the fewest 256-column groups
- *   per workgroup, a forced split (1..64) and forced waves per workgroup
- *   (1..16).  0 restores a value's default (environment SQLLM_TARGET_WGS,
- *   SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES, else built in).  sparse_naive
+ *   per workgroup, a forced split (1..16) and forced waves per workgroup
+ *   (1..16).  0 restores a value's built-in default (no environment
+ *   variable changes any launch).  sparse_naive
  *   = 1 switches the outliers to the unbalanced form for the ablation of the
  *   balanced kernel (summary page, Appendix C, Table C.1): one thread per
  *   row walks the row's nonzeros; 0 restores the balanced form.  dot_only =

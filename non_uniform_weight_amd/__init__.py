@@ -35,7 +35,7 @@ _lib.sqllm_packed_bytes.argtypes = [_i64, _i64, _i32]
 _lib.sqllm_workspace_bytes.restype = _sz
 _lib.sqllm_workspace_bytes.argtypes = [_i64, _i64, _i32]
 _lib.sqllm_pack.restype = _i32
-_lib.sqllm_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+_lib.sqllm_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _sz, _vp]
 _lib.sqllm_gemv.restype = _i32
 _lib.sqllm_gemv.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]
 _lib.sqllm_spmv_add.restype = _i32
@@ -164,8 +164,9 @@ def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None, stream
         out = torch.empty(n, dtype=torch.uint8, device=codes.device)
     if out.numel() < n:
         raise ValueError("pack: output buffer too small")
-    _check(_lib.sqllm_pack(_dev(codes, "codes", torch.uint8), rows, cols, bits, _dev(out, "packed", torch.uint8),
-                           _stream(stream)), "sqllm_pack")
+    cp, op = _dev(codes, "codes", torch.uint8), _dev(out, "packed", torch.uint8)
+    flag = _cached_workspace(256, codes.device, stream)  # the call's error flag; the call leaves it zero
+    _check(_lib.sqllm_pack(cp, rows, cols, bits, op, flag.data_ptr(), flag.numel(), _stream(stream)), "sqllm_pack")
     return out
 
 

@@ -12,10 +12,10 @@ using namespace sqllm;
 
 namespace {
 
-// Launch-shape knobs.  Defaults are built in; the environment (read once:
-// SQLLM_TARGET_WGS, SQLLM_MIN_GPS, SQLLM_SPLIT, SQLLM_WAVES)
-// or sqllm_test_tuning() may override them.  Every value gives the same
-// result within the stated tolerance (bit-identical while split <= 2).
+// Launch-shape knobs for tests and ablations only (sqllm_test_tuning); every
+// ordinary call uses the built-in defaults, and no environment variable
+// changes a launch.  Every value gives the same result within the stated
+// tolerance.
 struct Tuning {
     int target_wgs = 256;   // workgroups the column split aims for (one per compute unit)
     int min_gps = 8;        // fewest column groups per workgroup (pair-table build amortisation)
@@ -23,19 +23,6 @@ struct Tuning {
     int force_waves = 0;    // 0: choose; else waves per workgroup
     int sparse_naive = 0;   // ablation: 1 = outliers one lane per row, unbalanced
     int dot_only = 0;       // ablation: 1 = dense part in the v_dot2c form instead of the matrix cores
-    Tuning()
-    {
-        auto get = [](const char *name, int lo, int hi, int dflt) {
-            const char *v = getenv(name);
-            if (!v || !*v) return dflt;
-            long x = strtol(v, nullptr, 10);
-            return (x < lo || x > hi) ? dflt : (int)x;
-        };
-        target_wgs = get("SQLLM_TARGET_WGS", 1, 1 << 20, target_wgs);
-        min_gps = get("SQLLM_MIN_GPS", 1, 1 << 16, min_gps);
-        force_split = get("SQLLM_SPLIT", 1, kMaxSplit, 0);
-        force_waves = get("SQLLM_WAVES", 1, kMaxWaves, 0);
-    }
 };
 
 Tuning &tuning_state()
@@ -58,14 +45,21 @@ sqllm_status check_shape(int64_t rows, int64_t cols)
     return SQLLM_OK;
 }
 
-// One 8-byte (fp32 sum, count) word per (tile, batch column, row of tile),
-// then (from batch kXtBatch) x transposed for the outlier gathers.
-size_t slots_need(int64_t rows, int batch)
+// Combine words of a call whose row tiles are split over `split`
+// workgroups: split - 1 eight-byte words per (tile, batch column, row of
+// tile) (none at split 1).
+size_t words_need(int64_t rows, int batch, int split)
 {
-    return (size_t)tiles_of(rows) * (size_t)batch * kTileRows * 8;
+    return split > 1 ? (size_t)tiles_of(rows) * (size_t)(split - 1) * (size_t)batch * kTileRows * 8 : 0;
 }
 
-size_t workspace_need(int64_t rows, int64_t cols, int batch) { return slots_need(rows, batch) + xt_bytes(cols, batch); }
+// The workspace one product may need: the words of the largest split, then
+// (from batch kXtBatch) x transposed for the outlier gathers, always at that
+// offset (a call's words, and those of a row slice, stay below it).
+size_t workspace_need(int64_t rows, int64_t cols, int batch)
+{
+    return words_need(rows, batch, kMaxSplit) + xt_bytes(cols, batch);
+}
 
 // Outliers at batch >= kXtBatch whose x is not staged in LDS gather from a
 // transposed copy in the workspace (when the workspace has room for it):
@@ -132,7 +126,7 @@ int64_t fill_two_slots(GroupArgs &g, int64_t wgs, void *const *own_ws, const siz
     for (int k = 0; k < g.n; ++k) {
         KernelArgs &a = g.item[k];
         if (wgs + a.tiles > 2 * t || a.groups < 2 * tuning().min_gps) break;
-        if (!own_ws[k] || own_bytes[k] < slots_need(a.rows, batch)) break;
+        if (!own_ws[k] || own_bytes[k] < words_need(a.rows, batch, 2)) break;
         a.gps = (int)ceil_div(a.groups, 2);
         a.split = (int)ceil_div(a.groups, a.gps);
         wgs += (int64_t)a.tiles * (a.split - 1);
@@ -155,7 +149,7 @@ bool slice_for_two_slots(const KernelArgs &a, int bits, int batch, void *ws, siz
     if (tuning().force_split || tuning().force_waves || a.split != 1 || a.tiles <= t || a.tiles >= 2 * t) return false;
     const int h = (int)(2 * t - a.tiles);
     if (a.groups < 2 * tuning().min_gps) return false;
-    if (!ws || !aligned(ws, 256) || ws_bytes < slots_need((int64_t)h * kTileRows, batch)) return false;
+    if (!ws || !aligned(ws, 256) || ws_bytes < words_need((int64_t)h * kTileRows, batch, 2)) return false;
     const int64_t r0 = (int64_t)h * kTileRows;
     KernelArgs lo = a, hi = a;
     lo.rows = (int)r0;
@@ -251,7 +245,7 @@ sqllm_status sparse_checks(const int32_t *row_ptr, const uint16_t *col_idx, cons
 sqllm_status workspace_checks(int split, int64_t rows, int batch, void *ws, size_t ws_bytes)
 {
     if (split <= 1) return SQLLM_OK;
-    if (!ws || !aligned(ws, 256) || ws_bytes < slots_need(rows, batch)) return SQLLM_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256) || ws_bytes < words_need(rows, batch, split)) return SQLLM_ERR_WORKSPACE;
     return SQLLM_OK;
 }
 
@@ -271,7 +265,7 @@ void plan_xt(KernelArgs &a, int batch, int64_t nnz, int64_t nnz_x, void *ws, siz
             a.xt = jobs.xt[k];
             return;
         }
-    uint16_t *xt = (uint16_t *)((char *)ws + slots_need(a.rows, batch));
+    uint16_t *xt = (uint16_t *)((char *)ws + words_need(a.rows, batch, kMaxSplit));
     jobs.x[jobs.n] = a.x;
     jobs.xt[jobs.n] = xt;
     jobs.cols[jobs.n] = a.cols;
@@ -344,7 +338,7 @@ sqllm_status plan_group_pass(const sqllm_product *items, int n, int batch, bool 
         a.col = p.col_idx;
         a.val = p.val;
         choose_split(a, total_tiles);
-        if (a.split > 1 && (!workspace || left < slots_need(p.rows, batch))) return SQLLM_ERR_WORKSPACE;
+        if (a.split > 1 && (!workspace || left < words_need(p.rows, batch, a.split))) return SQLLM_ERR_WORKSPACE;
         own_ws[g.n] = mine;
         own_bytes[g.n] = left < need ? left : need;
         own_nnz[g.n] = p.nnz;
@@ -406,23 +400,28 @@ size_t sqllm_workspace_bytes(int64_t rows, int64_t cols, int batch)
     return workspace_need(rows, cols, batch);
 }
 
-sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed, hipStream_t stream)
+sqllm_status sqllm_pack(const uint8_t *codes, int64_t rows, int64_t cols, int bits, void *packed, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
 {
-    if (!codes || !packed) return SQLLM_ERR_NULL;
+    if (!codes || !packed || !workspace) return SQLLM_ERR_NULL;
     if (bits < 2 || bits > 4) return SQLLM_ERR_BITS;
     sqllm_status st = check_shape(rows, cols);
     if (st != SQLLM_OK) return st;
     if (!aligned(codes, 16) || !aligned(packed, 16)) return SQLLM_ERR_ALIGN;
-    int *bad = nullptr;
-    if (hipMalloc((void **)&bad, sizeof(int)) != hipSuccess) return SQLLM_ERR_HIP;
+    if (!aligned(workspace, 4) || workspace_bytes < 4) return SQLLM_ERR_WORKSPACE;
+    int *bad = (int *)workspace; // the caller's: the library allocates nothing
     int host_bad = 0;
-    bool ok = hipMemsetAsync(bad, 0, sizeof(int), stream) == hipSuccess &&
-              launch_pack(codes, (int)rows, (int)cols, bits, packed, bad, stream) == hipSuccess &&
-              hipMemcpyAsync(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost, stream) == hipSuccess &&
-              hipStreamSynchronize(stream) == hipSuccess;
-    (void)hipFree(bad);
+    const bool ok = hipMemsetAsync(bad, 0, sizeof(int), stream) == hipSuccess &&
+                    launch_pack(codes, (int)rows, (int)cols, bits, packed, bad, stream) == hipSuccess &&
+                    hipMemcpyAsync(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost, stream) == hipSuccess &&
+                    hipStreamSynchronize(stream) == hipSuccess;
     if (!ok) return SQLLM_ERR_HIP;
-    return host_bad ? SQLLM_ERR_CODE_RANGE : SQLLM_OK;
+    if (host_bad) { // leave the caller's word zero again (it may be a hot-call workspace)
+        if (hipMemsetAsync(bad, 0, sizeof(int), stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess)
+            return SQLLM_ERR_HIP;
+        return SQLLM_ERR_CODE_RANGE;
+    }
+    return SQLLM_OK;
 }
 
 sqllm_status sqllm_gemv(const void *packed, const uint16_t *lut, int bits, int64_t rows, int64_t cols,

@@ -45,10 +45,11 @@
 //
 // The waves' fp32 row sums are added in a fixed order; the sparse part joins
 // the dense part in fp32 before the single rounding (kernel fusion).  A row
-// tile's columns may be split over several workgroups: each adds its fp32
-// sums into a (sum, count) word per output with a compare-and-swap and the
-// one that completes the count rounds and writes y -- no fences or cache
-// flushes, one atomic round trip.
+// tile's columns may be split over several workgroups: their fp32 sums meet
+// in a binary tree of words in the workspace (see finish_rows), one atomic OR
+// per level, added in an order that does not depend on which workgroup
+// arrives first; the last one rounds and writes y -- no fences or cache
+// flushes.
 
 #ifndef SQLLM_DEVICE_H
 #define SQLLM_DEVICE_H
@@ -697,44 +698,52 @@ constexpr bool kRingAfterTable = true;
 // barrier.
 constexpr int kStageQuads = 4;
 
-// Round and store (or hand over) this workgroup's fp32 row sums.
+// Round and store (or hand over) this workgroup's fp32 row sums.  With the
+// row tile split over count > 1 workgroups (this one is split index s), the
+// partial sums meet in a binary tree of 64-bit words in the workspace, count
+// - 1 per (tile, batch column, row): at level 0 the partials of splits 2j and
+// 2j+1 share word j, each setting its half with one atomic OR (the fp32 bits
+// inverted, so that an empty half reads 0; -0.0 and +0.0 stay distinct); an
+// odd last one passes up unpaired.  The one that finds the other half already
+// there adds left + right, clears the word and goes on to the next level;
+// the last one rounds once and stores y.  Which workgroup arrives first does
+// not change any sum, so repeated launches give identical bits, and every
+// word is zero again when the launch has finished.
 template <int B, bool ADDY>
-__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int lane, const float *tot, int count)
+__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int s, int lane, const float *tot, int count)
 {
     const int row = t * 64 + lane;
-    if (count == 1) {
-        if (row < a.rows) {
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float v = tot[b];
-                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
-                a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
-            }
-        }
-        return;
-    }
-    // (fp32 sum | count << 32) per output; the empty word is 0.  -0.0 is the
-    // additive identity, so a lone partial keeps its sign of zero.  With two
-    // workgroups per tile the result does not depend on arrival order.
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        unsigned long long *slot = a.slots + ((int64_t)t * B + b) * 64 + lane;
-        unsigned long long expected = 0ull, desired = 0ull;
-        for (;;) {
-            const uint32_t cnt = (uint32_t)(expected >> 32);
-            const float sum = cnt ? __uint_as_float((uint32_t)expected) : -0.0f;
-            desired = ((unsigned long long)(cnt + 1) << 32) | __float_as_uint(sum + tot[b]);
-            const unsigned long long got = atomicCAS(slot, expected, desired);
-            if (got == expected) break;
-            expected = got;
-        }
-        if ((int)(desired >> 32) == count) {
-            if (row < a.rows) {
-                float v = __uint_as_float((uint32_t)desired);
-                if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
-                a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
+        float v = tot[b];
+        int i = s, m = count, base = 0;
+        bool last = true;
+        while (m > 1) {
+            if ((m & 1) && i == m - 1) { // unpaired: passes up as it is
+                i >>= 1;
+                base += m >> 1;
+                m = (m + 1) >> 1;
+                continue;
             }
-            __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned long long *w = a.slots + (((int64_t)t * (count - 1) + base + (i >> 1)) * B + b) * 64 + lane;
+            const uint32_t enc = ~__float_as_uint(v);
+            const unsigned long long mine = (i & 1) ? (unsigned long long)enc << 32 : (unsigned long long)enc;
+            const unsigned long long old = __hip_atomic_fetch_or(w, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t other = (i & 1) ? (uint32_t)old : (uint32_t)(old >> 32);
+            if (other == 0) { // the partner has not arrived: it goes on
+                last = false;
+                break;
+            }
+            const float o = __uint_as_float(~other);
+            v = (i & 1) ? o + v : v + o; // left + right
+            __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            i >>= 1;
+            base += m >> 1;
+            m = (m + 1) >> 1;
+        }
+        if (last && row < a.rows) {
+            if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
+            a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
         }
     }
 }
@@ -1009,7 +1018,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         for (int k = 0; k < W; ++k) v += red[(k * B + b) * 64 + lane];
         tot[b] = v;
     }
-    finish_rows<B, ADDY>(a, t, lane, tot, a.split);
+    finish_rows<B, ADDY>(a, t, s, lane, tot, a.split);
 }
 
 template <int BITS, int B, int MODE, bool MF>

@@ -14,7 +14,7 @@ constexpr int kGroupCols = 256;   // codes per group
 constexpr int kMaxBatch = 16;
 constexpr int kMaxDotBatch = 8;   // the v_dot2c form is built up to this batch; above it only the matrix cores
 constexpr int kMaxWaves = 16;     // waves per workgroup
-constexpr int kMaxSplit = 64;     // workgroups sharing one row tile
+constexpr int kMaxSplit = 16;     // workgroups sharing one row tile
 constexpr int kTableBytes = 256 * 64 * 4;           // pair table: 256 entries x 64 lanes x half2
 constexpr int kLdsBudget = 160 * 1024;              // LDS per compute unit on gfx950
 constexpr int kSparseShare = 512; // outlier nonzeros per wave the outlier-only kernel aims for
@@ -30,7 +30,7 @@ struct KernelArgs {
     const uint16_t *val;      // fp16 [nnz]
     const uint16_t *x;        // fp16 [batch][cols]
     uint16_t *y;              // fp16 [batch][rows]
-    unsigned long long *slots;  // workspace: one (fp32 sum, count) word per (tile, batch, row)
+    unsigned long long *slots;  // workspace: split - 1 combine words per (tile, batch, row)
     int rows, cols, tiles, groups;
     int ldy;                  // y's batch stride: rows, or more for a row slice of a larger product
     int split;                // workgroups per row tile

@@ -51,13 +51,15 @@ def test_size_queries(nwpkg):
     assert nwpkg.packed_bytes(64, 256, 1) == 0
     assert nwpkg.workspace_bytes(22016, 8192, 1) >= 344 * 4
     assert nwpkg.workspace_bytes(22016, 8192, 17) == 0
-    assert nwpkg.workspace_bytes(64, 8192, 12) == 12 * 64 * 8 + 8192 * 16 * 2
-    # (sum, count) words per output, then at batch >= 5 x transposed to [cols][8]
-    assert nwpkg.workspace_bytes(100, 256, 1) == 2 * 64 * 8
-    assert nwpkg.workspace_bytes(100, 256, 2) == 2 * 2 * 64 * 8
-    assert nwpkg.workspace_bytes(100, 256, 4) == 2 * 4 * 64 * 8
-    assert nwpkg.workspace_bytes(100, 256, 8) == 2 * 8 * 64 * 8 + 256 * 8 * 2
-    assert nwpkg.workspace_bytes(64, 8192, 5) == 5 * 64 * 8 + 8192 * 8 * 2
+    # combine words of the largest split (16 workgroups per row tile: 15 words
+    # per output), then at batch >= 5 x transposed to [cols][8] ([cols][16] above 8)
+    W15 = 15 * 64 * 8
+    assert nwpkg.workspace_bytes(64, 8192, 12) == 12 * W15 + 8192 * 16 * 2
+    assert nwpkg.workspace_bytes(100, 256, 1) == 2 * W15
+    assert nwpkg.workspace_bytes(100, 256, 2) == 2 * 2 * W15
+    assert nwpkg.workspace_bytes(100, 256, 4) == 2 * 4 * W15
+    assert nwpkg.workspace_bytes(100, 256, 8) == 2 * 8 * W15 + 256 * 8 * 2
+    assert nwpkg.workspace_bytes(64, 8192, 5) == 5 * W15 + 8192 * 8 * 2
 
 
 P = ctypes.c_void_p
@@ -120,11 +122,14 @@ def test_sparse_argument_errors(lib):
 
 
 def test_pack_and_reader_argument_errors(lib):
-    assert lib.sqllm_pack(None, 64, 256, 3, A16, None) == 1
-    assert lib.sqllm_pack(A16, 64, 256, 3, None, None) == 1
-    assert lib.sqllm_pack(A16, 64, 256, 7, B16, None) == 2
-    assert lib.sqllm_pack(A16, 64, 255, 3, B16, None) == 3
-    assert lib.sqllm_pack(P(0x100001), 64, 256, 3, B16, None) == 5
+    assert lib.sqllm_pack(None, 64, 256, 3, A16, B16, 256, None) == 1
+    assert lib.sqllm_pack(A16, 64, 256, 3, None, B16, 256, None) == 1
+    assert lib.sqllm_pack(A16, 64, 256, 3, B16, None, 256, None) == 1      # the error flag is the caller's
+    assert lib.sqllm_pack(A16, 64, 256, 7, B16, B16, 256, None) == 2
+    assert lib.sqllm_pack(A16, 64, 255, 3, B16, B16, 256, None) == 3
+    assert lib.sqllm_pack(P(0x100001), 64, 256, 3, B16, B16, 256, None) == 5
+    assert lib.sqllm_pack(A16, 64, 256, 3, B16, B16, 3, None) == 8         # flag word too small
+    assert lib.sqllm_pack(A16, 64, 256, 3, B16, MIS, 256, None) == 8       # flag word misaligned
     assert lib.sqllm_test_unpack(A16, 64, 256, 3, None, None) == 1
     assert lib.sqllm_test_decode(A16, None, 64, 256, 3, B16, None) == 1
     assert lib.sqllm_test_decode(A16, B16, 64, 256, 1, B16, None) == 2
@@ -172,7 +177,7 @@ def test_group_workspace_bytes(lib, nwpkg):
 
 
 def test_tuning_hook_bounds(lib):
-    assert lib.sqllm_test_tuning(0, 0, 65, 0, 0, 0) == 3      # split above 64
+    assert lib.sqllm_test_tuning(0, 0, 17, 0, 0, 0) == 3      # split above 16
     assert lib.sqllm_test_tuning(0, 0, 0, 17, 0, 0) == 3      # more than 16 waves
     assert lib.sqllm_test_tuning(0, 0, 0, 0, 2, 0) == 3       # outlier form 0 or 1
     assert lib.sqllm_test_tuning(0, 0, 0, 0, 0, 2) == 3       # dense form 0 or 1
@@ -349,6 +354,22 @@ def test_forced_shapes_turn_the_rules_off(nwpkg):
         assert [p["split"] for p in plans] == [1, 1, 1]
     finally:
         nwpkg.set_tuning()
+
+
+def test_environment_does_not_change_a_launch(nwpkg):
+    """Launch shapes come from the shapes alone: environment variables named like the knobs change nothing."""
+    import subprocess
+    import sys
+    code = ("import json, non_uniform_weight_amd as nw; "
+            "print(json.dumps([nw.launch_plan(s, batch=b) for s in ([(22016, 8192, 0)], [(8192, 8192, 30000)]) "
+            "for b in (1, 6)]))")
+    env = dict(os.environ, SQLLM_SPLIT="3", SQLLM_WAVES="4", SQLLM_TARGET_WGS="7", SQLLM_MIN_GPS="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True,
+                         timeout=120, check=True).stdout
+    import json
+    want = [nwpkg.launch_plan(s, batch=b) for s in ([(22016, 8192, 0)], [(8192, 8192, 30000)]) for b in (1, 6)]
+    assert json.loads(out.strip().splitlines()[-1]) == json.loads(json.dumps(want))
 
 
 def test_launch_plan_argument_errors(lib):

@@ -256,6 +256,53 @@ def test_repeated_calls_are_bit_identical():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("rows,cols,bits,zipf", [(4096, 11008, 4, False), (5120, 13824, 3, True)])
+@pytest.mark.parametrize("batch", [1, 6])
+def test_split_combine_is_deterministic(rows, cols, bits, zipf, batch):
+    """Down projections of LLaMA-7B and LLaMA-13B run split over many
+    workgroups per row tile; their partial sums meet in a fixed binary tree,
+    so repeated calls, with one workspace or another, give identical bits
+    whichever workgroup ends first."""
+    spec = synth.MatrixSpec("down", rows, cols, bits, batch, 45, zipf)
+    (plan,), _ = nw().launch_plan([(rows, cols, spec.nnz)], batch=batch)
+    assert plan["split"] > 1 or plan["slice_tiles"] > 0
+    step(f"determinism {rows}x{cols} bits {bits} batch {batch} plan {plan}")
+    m = synth.make_matrix(spec, seed=0, workload=2 if rows == 4096 else 3, index=1 if rows == 4096 else 6)
+    d = DevMatrix.from_synth(m)
+    ws2 = torch.zeros(nw().workspace_bytes(rows, cols, batch), dtype=torch.uint8, device="cuda")
+    outs = [dev_to_u16(d.fused()) for _ in range(4)] + [dev_to_u16(d.fused(ws=ws2)) for _ in range(2)]
+    for k, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"call {k} differs in {int((outs[0] != o).sum())} outputs"
+    assert int(ws2.view(torch.int32).abs().sum().item()) == 0
+    sel = np.sort(np.random.default_rng(stable_seed("det", rows, batch)).choice(rows, 512, replace=False))
+    y_ref, scale = oracle.dense_sparse_gemv(m.codes[sel], m.lut, bits, m.row_ptr, m.col, m.val, m.x, rows=rows,
+                                            sel=sel)
+    ok, worst = oracle.within_tolerance(outs[0][:, sel], y_ref, scale, TOL)
+    assert ok, f"max normalised error {worst:.3e}"
+
+
+def test_two_streams_default_workspaces():
+    """Calls without a workspace on two streams at once: each stream gets
+    its own cached workspace, and both results match the oracle."""
+    step("two streams, default workspaces")
+    rng = np.random.default_rng(12)
+    cases = [_make_case(rng, 4096, 8192, 3, 1, "5pct"), _make_case(rng, 8192, 4096, 3, 6, "5pct")]
+    mats = [DevMatrix(codes, lut, 3, rp, col, val, x) for codes, lut, x, rp, col, val in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    ys = [[], []]
+    for _ in range(3):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                ys[k].append(mats[k].fused())
+    torch.cuda.synchronize()
+    for k in range(2):
+        codes, lut, x, rp, col, val = cases[k]
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+        for y in ys[k]:
+            assert_close(y, y_ref, scale, TOL, f"stream {k}")
+
+
 def test_permuted_table_with_remapped_codes():
     """Permuting a row's table entries together with its codes leaves y unchanged."""
     step("lut permutation invariance")
