@@ -116,7 +116,8 @@ typedef enum {
     SQLLM_ERR_CODE_RANGE = 6, /* sqllm_pack: a code is >= 2^bits */
     SQLLM_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed */
     SQLLM_ERR_WORKSPACE = 8,  /* workspace missing, misaligned or too small */
-    SQLLM_ERR_CAPACITY = 9    /* sqllm_outlier_extract: more outliers than the CSR buffers hold */
+    SQLLM_ERR_CAPACITY = 9,   /* sqllm_outlier_extract: more outliers than the CSR buffers hold */
+    SQLLM_ERR_SCRATCH = 10    /* sqllm_dense_sparse_gemv_noalloc: the launch needs more than its fixed scratch */
 } sqllm_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -225,6 +226,37 @@ size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch)
 
 sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, int bits, int batch, void *workspace,
                                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sqllm_dense_sparse_gemv_noalloc -- sqllm_dense_sparse_gemv without a
+ * workspace argument, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, fixed serving loops,
+ * hosts that forbid allocation).  Same arguments (minus the workspace),
+ * checks, launch and result: for any shape it takes, its output equals
+ * sqllm_dense_sparse_gemv's with a workspace of sqllm_workspace_bytes()
+ * bit for bit.  The call itself allocates nothing.
+ *   Scratch: the words and the transposed x live in a device array of
+ *   SQLLM_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU
+ *   it runs on, from its first use there until the process ends.  The first
+ *   call on a GPU looks the array up and zero-fills it on `stream` (make that
+ *   first call outside graph capture, or the fill joins the captured graph);
+ *   each call leaves it zero again, as with a caller's workspace.
+ *   Size: at the library's own launch shapes every accepted shape fits (a
+ *   call splits at most 256 row tiles' worth of outputs, whose words take at
+ *   most 2 MiB at batch 16).  The transposed x of batch >= 5 is used only
+ *   when sqllm_workspace_bytes(rows, cols, batch) <= the scratch size; larger
+ *   products read x in place (same result).  A launch that needs more words
+ *   than the scratch holds (only a launch shape forced through
+ *   sqllm_test_tuning) is refused with SQLLM_ERR_SCRATCH before any launch.
+ *   Concurrency: all calls on one GPU share its array.  Calls on one stream
+ *   are safe; calls that can overlap on the GPU (several streams, several
+ *   host threads with their own streams) race and give wrong results.
+ */
+#define SQLLM_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+sqllm_status sqllm_dense_sparse_gemv_noalloc(const void *packed, const uint16_t *lut, int bits,
+                                             const int32_t *row_ptr, const uint16_t *col_idx, const uint16_t *val,
+                                             int64_t nnz, int64_t rows, int64_t cols, const uint16_t *x, int batch,
+                                             uint16_t *y, hipStream_t stream);
 
 /*
  * Offline steps upstream of the product (not timed on the hot path): the

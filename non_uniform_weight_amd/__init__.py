@@ -43,6 +43,9 @@ _lib.sqllm_spmv_add.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
 _lib.sqllm_dense_sparse_gemv.restype = _i32
 _lib.sqllm_dense_sparse_gemv.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
                                          _sz, _vp]
+_lib.sqllm_dense_sparse_gemv_noalloc.restype = _i32
+_lib.sqllm_dense_sparse_gemv_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
+                                                 _vp]
 
 
 class Product(ctypes.Structure):
@@ -80,7 +83,7 @@ EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes",
            "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_group_workspace_bytes",
            "sqllm_dense_sparse_gemv_group", "sqllm_quantize_workspace_bytes", "sqllm_outlier_thresholds",
            "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning",
-           "sqllm_test_launch_plan")
+           "sqllm_test_launch_plan", "sqllm_dense_sparse_gemv_noalloc")
 MAX_GROUP = 8
 
 SQLLM_OK = 0
@@ -223,6 +226,21 @@ def dense_sparse_gemv(packed, lut, bits, row_ptr, col, val, x, y=None, ws=None, 
                                         rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
                                         _dev(y, "y", torch.float16), _dev(ws, "workspace", torch.uint8), ws.numel(),
                                         _stream(stream)), "sqllm_dense_sparse_gemv")
+    return y
+
+
+def dense_sparse_gemv_noalloc(packed, lut, bits, row_ptr, col, val, x, y, stream=None) -> torch.Tensor:
+    """y = (D + S) x with the library's fixed per-GPU scratch instead of a
+    workspace; y must be given (nothing is allocated on this path)."""
+    rows = lut.shape[0]
+    if y is None:
+        raise ValueError("dense_sparse_gemv_noalloc: y must be given")
+    x, y, batch, cols = _x_y(x, y, rows)
+    rp, ci, cv, nnz = _csr_ptrs(row_ptr, col, val)
+    _check(_lib.sqllm_dense_sparse_gemv_noalloc(_dev(packed, "packed", torch.uint8), _dev(lut, "lut", torch.float16),
+                                                bits, rp, ci, cv, nnz, rows, cols, _dev(x, "x", torch.float16), batch,
+                                                _dev(y, "y", torch.float16), _stream(stream)),
+           "sqllm_dense_sparse_gemv_noalloc")
     return y
 
 

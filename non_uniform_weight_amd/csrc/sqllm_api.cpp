@@ -384,6 +384,7 @@ const char *sqllm_status_string(sqllm_status s)
     case SQLLM_ERR_HIP: return "SQLLM_ERR_HIP: HIP runtime or launch failure";
     case SQLLM_ERR_WORKSPACE: return "SQLLM_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case SQLLM_ERR_CAPACITY: return "SQLLM_ERR_CAPACITY: more outliers than the CSR buffers hold";
+    case SQLLM_ERR_SCRATCH: return "SQLLM_ERR_SCRATCH: the launch needs more than the fixed 16 MiB scratch";
     }
     return "SQLLM_ERR_UNKNOWN";
 }

@@ -29,14 +29,14 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         assert lib.sqllm_status_string(code).startswith(b"SQLLM_")
     assert lib.sqllm_status_string(99) == b"SQLLM_ERR_UNKNOWN"
 
@@ -119,6 +119,32 @@ def test_sparse_argument_errors(lib):
     assert spmv(lib, x=MIS) == 5
     # no outliers: nothing to do, no HIP call, CSR pointers may be NULL
     assert spmv(lib, rp=None, col=None, val=None, nnz=0) == 0
+
+
+def test_noalloc_shape_errors_before_any_device_call(lib):
+    """Rows, columns or batch out of range come back before the entry point looks up its scratch."""
+    f = lib.sqllm_dense_sparse_gemv_noalloc
+    f.argtypes = [P, P, ctypes.c_int, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_int, P, P]
+    assert f(A16, A16, 3, None, None, None, 0, 0, 256, B16, 1, B16, None) == 3
+    assert f(A16, A16, 3, None, None, None, 0, 64, 300, B16, 1, B16, None) == 3
+    assert f(A16, A16, 3, None, None, None, 0, 64, 256, B16, 17, B16, None) == 4
+    assert f(A16, A16, 3, None, None, None, 0, 64, 256, B16, 0, B16, None) == 4
+
+
+def test_noalloc_words_fit_the_scratch(nwpkg):
+    """At the default launch shapes no accepted shape needs more than 2 MiB of
+    combine words (at most about 256 row tiles are split, into two), so the
+    16 MiB scratch of sqllm_dense_sparse_gemv_noalloc holds every call's words."""
+    scratch = 16 << 20
+    worst = 0
+    for rows in [*range(1, 3000, 37), *range(3000, 70000, 997), 1 << 20, (1 << 22) + 5]:
+        for cols in (256, 4096, 22016, 65536):
+            for batch in (1, 4, 5, 8, 9, 16):
+                for nnz in (0, 500000):
+                    (p,), _ = nwpkg.launch_plan([(rows, cols, nnz)], batch=batch, workspace_bytes=scratch)
+                    tiles = p["slice_tiles"] or (rows + 63) // 64
+                    worst = max(worst, tiles * (p["split"] - 1) * batch * 64 * 8)
+    assert 0 < worst <= 2 << 20
 
 
 def test_pack_and_reader_argument_errors(lib):
