@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-single", action="store_true",
                    help="skip the one-call-per-product pass, so that a profiler sees only the group launches")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
+    p.add_argument("--no-per-matrix", action="store_true",
+                   help="skip the cold single-matrix timings of the 7B, 7B-MLP, 13B and 65B shapes at batch 1")
     p.add_argument("--ablation", choices=("outliers", "batch", "offline", "configs"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
@@ -394,6 +396,121 @@ def batch_ablation(args) -> None:
           flush=True)
 
 
+def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per_trial: int = 200,
+                         trials: int = 5, full: bool = False) -> dict:
+    """One matrix of a single-matrix workload, one fused sqllm_dense_sparse_gemv
+    per product.  Cold: every call reads its own copy of codes, tables and CSR
+    (copies >= 1 GB, beyond the caches), calls_per_trial calls captured in a
+    HIP graph, median of `trials` replays.  full: also a plain launch loop
+    (arguments marshalled once, one C-ABI call per product) and warm (every
+    call on one copy)."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import non_uniform_weight_amd as nw
+    import synth
+
+    h = vp_stream(stream)
+    fn = nw.library().sqllm_dense_sparse_gemv
+    vp = ctypes.c_void_p
+    m = synth.make_matrix(spec, seed=seed, workload=wl, index=index)
+    packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
+    lut = torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16)
+    rp = torch.from_numpy(m.row_ptr).cuda()
+    col = torch.from_numpy(m.col.view(np.int16)).cuda()
+    val = torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16)
+    x = torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16)
+    y = torch.empty((spec.batch, spec.rows), dtype=torch.float16, device="cuda")
+    ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, spec.batch), 256), dtype=torch.uint8,
+                     device="cuda")
+    nnz = int(m.col.size)
+    del m
+    nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, nnz, spec.batch)
+    reps = max(1, -(-1024 * 2 ** 20 // nbytes))
+    copies = [(packed, lut, rp, col, val)] + [tuple(t.clone() for t in (packed, lut, rp, col, val))
+                                              for _ in range(reps - 1)]
+    argv = [(vp(c[0].data_ptr()), vp(c[1].data_ptr()), spec.bits, vp(c[2].data_ptr()), vp(c[3].data_ptr()),
+             vp(c[4].data_ptr()), nnz, spec.rows, spec.cols, vp(x.data_ptr()), spec.batch, vp(y.data_ptr()),
+             vp(ws.data_ptr()), ws.numel()) for c in copies]
+
+    def run(k, cold=True):
+        st = fn(*argv[k % reps if cold else 0], h)
+        if st != 0:
+            raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
+
+    def graph_us(cold):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(calls_per_trial):
+                run(k, cold)
+        ts = []
+        with torch.cuda.stream(stream):
+            g.replay()  # warm-up
+            torch.cuda.synchronize()
+            for _ in range(trials):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
+        del g
+        return statistics.median(ts)
+
+    def plain_us():
+        ts = []
+        with torch.cuda.stream(stream):
+            for k in range(20):
+                run(k)
+            torch.cuda.synchronize()
+            for _ in range(trials):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for k in range(calls_per_trial):
+                    run(k)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
+        return statistics.median(ts)
+
+    cold = graph_us(True)
+    ideal = nbytes / (HBM_PEAK_GBS * 1e3)
+    res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "bits": spec.bits,
+           "batch": spec.batch, "nnz": nnz, "bytes": nbytes, "copies": reps,
+           "ideal_us": round(ideal, 3), "target70_us": round(ideal / 0.7, 3),
+           "graph_us": round(cold, 3), "GB_per_s": round(nbytes / (cold * 1e3), 1),
+           "pct_peak": round(100 * ideal / cold, 1)}
+    if full:
+        plain, warm = plain_us(), graph_us(False)
+        res.update({"plain_us": round(plain, 3), "warm_us": round(warm, 3),
+                    "warm_GB_per_s": round(nbytes / (warm * 1e3), 1)})
+    del copies, argv, packed, lut, rp, col, val, x, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def per_matrix(seed: int, stream) -> dict:
+    """The single-matrix workloads at batch 1, cold (copies >= 1 GB), one
+    fused call per product in a HIP graph: LLaMA-7B q_proj 4096x4096 3-bit,
+    the 7B MLP pair up 11008x4096 + down 4096x11008 4-bit, the LLaMA-13B
+    layer's seven linears 3-bit with Zipf rows, and the LLaMA-65B shapes
+    8192x8192, 22016x8192, 8192x22016 3-bit; all with 0.45% outliers."""
+    import synth
+
+    names = {1: "llama7b", 2: "llama7b_mlp", 3: "llama13b", 4: "llama65b"}
+    out = {}
+    for wl in (1, 2, 3, 4):
+        for i, spec in enumerate(synth.workload(wl, batch=1) if wl == 4 else synth.workload(wl)):
+            r = single_matrix_timing(spec, wl, i, seed, stream)
+            key = f"{names[wl]}_{spec.name}_{spec.rows}x{spec.cols}_{spec.bits}bit"
+            out[key] = {"us_per_gemv": r["graph_us"], "GB_per_s": r["GB_per_s"],
+                        "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "nnz": r["nnz"], "copies": r["copies"]}
+            log(f"per matrix {key}: {r['graph_us']:.2f} us, {r['GB_per_s']:.0f} GB/s")
+    return out
+
+
 def config_table(args) -> None:
     """Each matrix of the four single-matrix workloads, one fused call per
     product: the 7B q_proj 4096x4096 (3-bit), the 7B MLP pair up 11008x4096 +
@@ -415,7 +532,6 @@ def config_table(args) -> None:
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
     h = vp_stream(stream)
-    fn = nw.library().sqllm_dense_sparse_gemv
     vp = ctypes.c_void_p
     calls_per_trial, trials = 200, 5
     cases = [(1, s) for s in synth.workload(1)] + [(2, s) for s in synth.workload(2)]
@@ -424,77 +540,9 @@ def config_table(args) -> None:
     out = []
     for wl, spec in cases:
         index = [s.name for s in synth.workload(wl, batch=spec.batch)].index(spec.name)
-        m = synth.make_matrix(spec, seed=args.seed, workload=wl, index=index)
-        packed = nw.pack(torch.from_numpy(m.codes).cuda(), spec.bits)
-        lut = torch.from_numpy(m.lut.view(np.int16)).cuda().view(torch.float16)
-        rp = torch.from_numpy(m.row_ptr).cuda()
-        col = torch.from_numpy(m.col.view(np.int16)).cuda()
-        val = torch.from_numpy(m.val.view(np.int16)).cuda().view(torch.float16)
-        x = torch.from_numpy(m.x.view(np.int16)).cuda().view(torch.float16)
-        y = torch.empty((spec.batch, spec.rows), dtype=torch.float16, device="cuda")
-        ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, spec.batch), 256), dtype=torch.uint8,
-                         device="cuda")
-        nnz = int(m.col.size)
-        nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, nnz, spec.batch)
-        reps = max(1, -(-1024 * 2 ** 20 // nbytes))
-        copies = [(packed, lut, rp, col, val)] + [tuple(t.clone() for t in (packed, lut, rp, col, val))
-                                                  for _ in range(reps - 1)]
-        argv = [(vp(c[0].data_ptr()), vp(c[1].data_ptr()), spec.bits, vp(c[2].data_ptr()), vp(c[3].data_ptr()),
-                 vp(c[4].data_ptr()), nnz, spec.rows, spec.cols, vp(x.data_ptr()), spec.batch, vp(y.data_ptr()),
-                 vp(ws.data_ptr()), ws.numel()) for c in copies]
-
-        def run(k, cold=True):
-            st = fn(*argv[k % reps if cold else 0], h)
-            if st != 0:
-                raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
-
-        def graph_us(cold):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for k in range(calls_per_trial):
-                    run(k, cold)
-            ts = []
-            with torch.cuda.stream(stream):
-                g.replay()  # warm-up: 200 calls
-                torch.cuda.synchronize()
-                for _ in range(trials):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    g.replay()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
-            del g
-            return statistics.median(ts)
-
-        def plain_us():
-            ts = []
-            with torch.cuda.stream(stream):
-                for k in range(20):
-                    run(k)
-                torch.cuda.synchronize()
-                for _ in range(trials):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for k in range(calls_per_trial):
-                        run(k)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(e0.elapsed_time(e1) * 1e3 / calls_per_trial)
-            return statistics.median(ts)
-
-        cold, plain, warm = graph_us(True), plain_us(), graph_us(False)
-        ideal = nbytes / (HBM_PEAK_GBS * 1e3)
-        res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "bits": spec.bits,
-               "batch": spec.batch, "nnz": nnz, "bytes": nbytes, "copies": reps,
-               "ideal_us": round(ideal, 3), "target70_us": round(ideal / 0.7, 3),
-               "graph_us": round(cold, 3), "GB_per_s": round(nbytes / (cold * 1e3), 1),
-               "pct_peak": round(100 * ideal / cold, 1), "plain_us": round(plain, 3),
-               "warm_us": round(warm, 3), "warm_GB_per_s": round(nbytes / (warm * 1e3), 1)}
+        res = single_matrix_timing(spec, wl, index, args.seed, stream, calls_per_trial, trials, full=True)
         log(f"config {res}")
         out.append(res)
-        del copies, argv, packed, lut, rp, col, val
-        torch.cuda.empty_cache()
     # the 13B layer as a decoder layer issues it: one group launch per (q,k,v), (o), (gate,up), (down),
     # every layer-sized copy of the seven products read once per 200 launches
     specs3 = synth.workload(3)
@@ -708,17 +756,21 @@ def main():
         kernel = (f"dense_sparse_kernel<{args.bits},1,fused,matrix>, 22016-row products "
                   f"dense_sparse_group_kernel<{args.bits},1,fused,matrix>")
 
-    value = ws.bytes_per_step / (ms * 1e-3) / 1e9
+    bytes_per_step = ws.bytes_per_step
+    value = bytes_per_step / (ms * 1e-3) / 1e9
     # level launches all run the group kernel; its average duration is the
     # timed region's length over the launches in it
     avg_launch_ms = ms / n_launches
-    avg_bytes = ws.bytes_per_step / n_launches
+    avg_bytes = bytes_per_step / n_launches
     achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
     log(f"per launch: {avg_launch_ms * 1e3:.2f} us avg, {achieved:.0f} GB/s")
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
     traffic = measured_traffic(kernel) if args.bits == 3 and args.density_bp == 45 else None
+    del ws
+    torch.cuda.empty_cache()
+    matrices = None if args.no_per_matrix else per_matrix(args.seed, stream)
     cpu = None
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
@@ -746,13 +798,13 @@ def main():
             "outlier_density_pct": args.density_bp / 100,
             "batch": 1,
             "gemvs_per_step": n_products,
-            "bytes_per_step": ws.bytes_per_step,
+            "bytes_per_step": bytes_per_step,
             "launch": mode + (", one group launch per (q,k,v), (o), (gate,up), (down)" if args.launch == "level"
                               else ", one call per product"),
         },
         "us_per_gemv": round(ms * 1e3 / n_products, 3),
         "single_calls": None if single_ms is None else {
-            "value": round(ws.bytes_per_step / (single_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "value": round(bytes_per_step / (single_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "us_per_gemv": round(single_ms * 1e3 / n_products, 3)},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {
@@ -767,6 +819,7 @@ def main():
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": round(avg_bytes),
         },
+        "per_matrix": matrices,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
