@@ -272,7 +272,7 @@ def outlier_ablation(args) -> None:
 
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    modes = ("dense_only", "balanced", "one_thread_per_row", "stream_ordered")
+    modes = ("dense_only", "balanced", "balanced_group", "balanced_planned", "one_thread_per_row", "stream_ordered")
     rows_out = []
     for wl, specs in ((3, synth.workload(3)), (4, synth.workload(4, batch=1))):
         for i, spec in enumerate(specs):
@@ -290,7 +290,10 @@ def outlier_ablation(args) -> None:
             y = torch.empty((1, spec.rows), dtype=torch.float16, device="cuda")
             ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, 1), 256), dtype=torch.uint8,
                              device="cuda")
-            res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "nnz": int(m.col.size)}
+            plan_host = nw.outlier_plan(m.row_ptr)
+            plan = torch.from_numpy(plan_host).cuda()
+            res = {"workload": wl, "product": spec.name, "shape": f"{spec.rows}x{spec.cols}", "nnz": int(m.col.size),
+                   "plan_helpers": int(plan_host[0])}
             for mode in modes:
                 def call(c):
                     if mode == "dense_only":
@@ -298,6 +301,11 @@ def outlier_ablation(args) -> None:
                     elif mode == "stream_ordered":
                         nw.gemv(c["packed"], c["lut"], spec.bits, x, y=y, ws=ws, stream=stream)
                         nw.spmv_add(c["row_ptr"], c["col"], c["val"], x, y, ws=ws, stream=stream)
+                    elif mode == "balanced_group":  # a group of one product, without the plan
+                        nw.dense_sparse_gemv_group([dict(c, x=x, y=y)], spec.bits, ws=ws, stream=stream)
+                    elif mode == "balanced_planned":  # the same with the outlier plan
+                        nw.dense_sparse_gemv_group([dict(c, x=x, y=y, plan=plan, plan_helpers=int(plan_host[0]))],
+                                                   spec.bits, ws=ws, stream=stream)
                     else:
                         nw.dense_sparse_gemv(c["packed"], c["lut"], spec.bits, c["row_ptr"], c["col"], c["val"], x,
                                              y=y, ws=ws, stream=stream)
@@ -397,13 +405,14 @@ def batch_ablation(args) -> None:
 
 
 def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per_trial: int = 200,
-                         trials: int = 5, full: bool = False) -> dict:
+                         trials: int = 5, full: bool = False, planned: bool = False) -> dict:
     """One matrix of a single-matrix workload, one fused sqllm_dense_sparse_gemv
     per product.  Cold: every call reads its own copy of codes, tables and CSR
     (copies >= 1 GB, beyond the caches), calls_per_trial calls captured in a
     HIP graph, median of `trials` replays.  full: also a plain launch loop
     (arguments marshalled once, one C-ABI call per product) and warm (every
-    call on one copy)."""
+    call on one copy).  planned: each call is a group call of this one
+    product with its outlier plan (sqllm_outlier_plan) instead."""
     import statistics
 
     import numpy as np
@@ -426,6 +435,7 @@ def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per
     ws = torch.zeros(max(nw.workspace_bytes(spec.rows, spec.cols, spec.batch), 256), dtype=torch.uint8,
                      device="cuda")
     nnz = int(m.col.size)
+    plan_host = nw.outlier_plan(m.row_ptr) if planned else None
     del m
     nbytes = nw.algorithmic_bytes(spec.rows, spec.cols, spec.bits, nnz, spec.batch)
     reps = max(1, -(-1024 * 2 ** 20 // nbytes))
@@ -434,11 +444,25 @@ def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per
     argv = [(vp(c[0].data_ptr()), vp(c[1].data_ptr()), spec.bits, vp(c[2].data_ptr()), vp(c[3].data_ptr()),
              vp(c[4].data_ptr()), nnz, spec.rows, spec.cols, vp(x.data_ptr()), spec.batch, vp(y.data_ptr()),
              vp(ws.data_ptr()), ws.numel()) for c in copies]
+    if planned:
+        plan = torch.from_numpy(plan_host).cuda()
+        gfn = nw.library().sqllm_dense_sparse_gemv_group
+        garr = []
+        for c in copies:
+            arr = (nw.Product * 1)()
+            arr[0] = nw.Product(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr(), c[3].data_ptr(), c[4].data_ptr(),
+                                nnz, spec.rows, spec.cols, x.data_ptr(), y.data_ptr(), plan.data_ptr(),
+                                int(plan_host[0]))
+            garr.append(arr)
 
     def run(k, cold=True):
-        st = fn(*argv[k % reps if cold else 0], h)
+        i = k % reps if cold else 0
+        if planned:
+            st = gfn(garr[i], 1, spec.bits, spec.batch, vp(ws.data_ptr()), ws.numel(), h)
+        else:
+            st = fn(*argv[i], h)
         if st != 0:
-            raise RuntimeError(f"sqllm_dense_sparse_gemv failed with status {st}")
+            raise RuntimeError(f"sqllm_dense_sparse_gemv{'_group' if planned else ''} failed with status {st}")
 
     def graph_us(cold):
         g = torch.cuda.CUDAGraph()
@@ -482,11 +506,15 @@ def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per
            "ideal_us": round(ideal, 3), "target70_us": round(ideal / 0.7, 3),
            "graph_us": round(cold, 3), "GB_per_s": round(nbytes / (cold * 1e3), 1),
            "pct_peak": round(100 * ideal / cold, 1)}
+    if planned:
+        res["plan_helpers"] = int(plan_host[0])
     if full:
         plain, warm = plain_us(), graph_us(False)
         res.update({"plain_us": round(plain, 3), "warm_us": round(warm, 3),
                     "warm_GB_per_s": round(nbytes / (warm * 1e3), 1)})
     del copies, argv, packed, lut, rp, col, val, x, y, ws
+    if planned:
+        del garr, plan
     torch.cuda.empty_cache()
     return res
 
@@ -508,6 +536,13 @@ def per_matrix(seed: int, stream) -> dict:
             out[key] = {"us_per_gemv": r["graph_us"], "GB_per_s": r["GB_per_s"],
                         "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "nnz": r["nnz"], "copies": r["copies"]}
             log(f"per matrix {key}: {r['graph_us']:.2f} us, {r['GB_per_s']:.0f} GB/s")
+            if wl == 3:  # the skewed rows, with the outlier plan (a group call of one product)
+                r = single_matrix_timing(spec, wl, i, seed, stream, planned=True)
+                out[key + "_planned"] = {"us_per_gemv": r["graph_us"], "GB_per_s": r["GB_per_s"],
+                                         "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "nnz": r["nnz"],
+                                         "copies": r["copies"], "plan_helpers": r["plan_helpers"]}
+                log(f"per matrix {key}_planned: {r['graph_us']:.2f} us, {r['GB_per_s']:.0f} GB/s, "
+                    f"{r['plan_helpers']} helpers")
     return out
 
 

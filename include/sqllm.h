@@ -202,6 +202,10 @@ sqllm_status sqllm_dense_sparse_gemv(const void *packed, const uint16_t *lut, in
  *          holds device pointers laid out as for sqllm_dense_sparse_gemv,
  *          nnz == 0 allowed (row_ptr / col_idx / val may then be NULL).
  *          No product's y may overlap any product's inputs or another y.
+ *          plan / plan_helpers: see sqllm_outlier_plan below (NULL / 0: no
+ *          plan; a plan with plan_helpers > 0 needs a NULL-free plan, 4-byte
+ *          aligned, plan_helpers <= 8 * ceil(rows / 64), else
+ *          SQLLM_ERR_NULL / SQLLM_ERR_ALIGN / SQLLM_ERR_SHAPE).
  *   workspace: at least sqllm_group_workspace_bytes(items, n, batch) bytes,
  *          256-byte aligned, zero-filled before first use, left zeroed; the
  *          products use disjoint parts of it in item order.
@@ -220,9 +224,44 @@ typedef struct {
     int64_t cols;
     const uint16_t *x;        /* fp16 [batch][cols], 16-byte aligned */
     uint16_t *y;              /* fp16 [batch][rows], overwritten */
+    const int32_t *plan;      /* device copy of sqllm_outlier_plan's output for this CSR, or NULL */
+    int64_t plan_helpers;     /* plan[0]: the plan's extra workgroups (0 without a plan) */
 } sqllm_product;
 
 size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch);
+
+/*
+ * sqllm_outlier_plan -- offline, host only: the preprocessing step of the
+ * balanced sparse kernel (§3.4 "Kernel Implementation": a fixed share of the
+ * nonzeros per thread, decided ahead of time; Appendix C, Figure C.1: a few
+ * output channels hold far more outliers than the rest).  The product
+ * kernels share a row tile's nonzeros evenly among the workgroups that own
+ * the tile; a tile holding far more than the others would keep its
+ * workgroups busy after the rest have finished.  The plan gives such tiles
+ * extra workgroups ("helpers") that take shares of the tile's nonzeros and
+ * nothing else, and whose partial sums join the tile's fixed-order combine.
+ *   Rule: with tiles = ceil(rows / 64) and q = 2 * ceil(nnz / tiles), tile t
+ *   holding n_t > q nonzeros gets min(8, ceil(n_t / q) - 1) helpers.
+ *   row_ptr: HOST int32 [rows + 1], the CSR's row pointers (row_ptr[0] == 0,
+ *            non-decreasing); read only.
+ *   plan:    HOST int32 buffer of plan_len entries.  Written: plan[0] = H,
+ *            the number of helpers; plan[1 + t] = helpers of tile t (0..8);
+ *            then H entries (t << 4) | e, e = 0 .. helpers of t - 1, in
+ *            tile order.
+ *   Returns the entries written (1 + tiles + H), or 0 when an argument is
+ *   out of range (rows < 1, a NULL pointer, row pointers not
+ *   non-decreasing from 0) or plan_len is below sqllm_outlier_plan_len().
+ * The caller copies the plan to the device (int32, 4-byte aligned) and sets
+ * sqllm_product.plan and .plan_helpers = plan[0] for the group call.  A
+ * planned product needs the full sqllm_workspace_bytes() region (its tiles
+ * combine up to 16 partial sums), runs its row tiles over at most 8
+ * workgroups each besides the helpers, and gives the same result as without
+ * the plan within the stated tolerance; repeated calls give identical bits.
+ * A plan with no helpers changes nothing.  The single-product calls take no
+ * plan; a group of one product does.
+ */
+size_t sqllm_outlier_plan_len(int64_t rows);
+size_t sqllm_outlier_plan(const int32_t *row_ptr, int64_t rows, int32_t *plan, size_t plan_len);
 
 sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, int bits, int batch, void *workspace,
                                            size_t workspace_bytes, hipStream_t stream);

@@ -17,6 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch  # loads the HIP runtime first, so libsqllm.so binds to the same one
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -51,9 +52,13 @@ _lib.sqllm_dense_sparse_gemv_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, 
 class Product(ctypes.Structure):
     """One item of sqllm_dense_sparse_gemv_group (sqllm_product)."""
     _fields_ = [("packed", _vp), ("lut", _vp), ("row_ptr", _vp), ("col_idx", _vp), ("val", _vp), ("nnz", _i64),
-                ("rows", _i64), ("cols", _i64), ("x", _vp), ("y", _vp)]
+                ("rows", _i64), ("cols", _i64), ("x", _vp), ("y", _vp), ("plan", _vp), ("plan_helpers", _i64)]
 
 
+_lib.sqllm_outlier_plan_len.restype = _sz
+_lib.sqllm_outlier_plan_len.argtypes = [_i64]
+_lib.sqllm_outlier_plan.restype = _sz
+_lib.sqllm_outlier_plan.argtypes = [_vp, _i64, _vp, _sz]
 _lib.sqllm_group_workspace_bytes.restype = _sz
 _lib.sqllm_group_workspace_bytes.argtypes = [ctypes.POINTER(Product), _i32, _i32]
 _lib.sqllm_dense_sparse_gemv_group.restype = _i32
@@ -83,7 +88,8 @@ EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes",
            "sqllm_spmv_add", "sqllm_dense_sparse_gemv", "sqllm_group_workspace_bytes",
            "sqllm_dense_sparse_gemv_group", "sqllm_quantize_workspace_bytes", "sqllm_outlier_thresholds",
            "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning",
-           "sqllm_test_launch_plan", "sqllm_dense_sparse_gemv_noalloc")
+           "sqllm_test_launch_plan", "sqllm_dense_sparse_gemv_noalloc", "sqllm_outlier_plan_len",
+           "sqllm_outlier_plan")
 MAX_GROUP = 8
 
 SQLLM_OK = 0
@@ -244,9 +250,27 @@ def dense_sparse_gemv_noalloc(packed, lut, bits, row_ptr, col, val, x, y, stream
     return y
 
 
+def outlier_plan(row_ptr) -> np.ndarray:
+    """Offline: the outlier plan of a CSR (sqllm_outlier_plan) from its row
+    pointers (host array or tensor, int32 [rows + 1]); int32 entries, the
+    helper count first.  Copy it to the device for a group item's "plan"."""
+    rp = np.ascontiguousarray(row_ptr.cpu().numpy() if isinstance(row_ptr, torch.Tensor) else row_ptr,
+                              dtype=np.int32)
+    rows = rp.size - 1
+    cap = int(_lib.sqllm_outlier_plan_len(rows))
+    if cap == 0:
+        raise ValueError(f"outlier_plan: unsupported row count {rows}")
+    out = np.zeros(cap, dtype=np.int32)
+    n = int(_lib.sqllm_outlier_plan(rp.ctypes.data, rows, out.ctypes.data, cap))
+    if n == 0:
+        raise ValueError("outlier_plan: row pointers must start at 0 and never decrease")
+    return out[:n]
+
+
 def group_products(items, bits: int):
     """ctypes array of sqllm_product from dicts with keys packed, lut, row_ptr,
-    col, val, x, y (tensors; row_ptr/col/val may be None)."""
+    col, val, x, y (tensors; row_ptr/col/val may be None) and optionally plan
+    (device int32 tensor from outlier_plan)."""
     arr = (Product * len(items))()
     batch = None
     for k, it in enumerate(items):
@@ -256,8 +280,13 @@ def group_products(items, bits: int):
             raise ValueError("group: every product must have the same batch")
         batch = b
         rp, ci, cv, nnz = _csr_ptrs(it.get("row_ptr"), it.get("col"), it.get("val"))
+        plan = it.get("plan")
+        pp, ph = None, 0
+        if plan is not None:
+            pp = _dev(plan, "plan", torch.int32)
+            ph = int(it["plan_helpers"]) if "plan_helpers" in it else int(plan[0].item())  # the latter syncs
         arr[k] = Product(_dev(it["packed"], "packed", torch.uint8), _dev(it["lut"], "lut", torch.float16), rp, ci, cv,
-                         nnz, rows, cols, _dev(x, "x", torch.float16), _dev(y, "y", torch.float16))
+                         nnz, rows, cols, _dev(x, "x", torch.float16), _dev(y, "y", torch.float16), pp, ph)
     return arr, batch
 
 

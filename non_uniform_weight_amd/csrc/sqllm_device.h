@@ -699,48 +699,66 @@ constexpr bool kRingAfterTable = true;
 constexpr int kStageQuads = 4;
 
 // Round and store (or hand over) this workgroup's fp32 row sums.  With the
-// row tile split over count > 1 workgroups (this one is split index s), the
-// partial sums meet in a binary tree of 64-bit words in the workspace, count
-// - 1 per (tile, batch column, row): at level 0 the partials of splits 2j and
+// row tile split over several workgroups (this one is leaf s), the partial
+// sums meet in a binary tree of 64-bit words in the workspace, one word per
+// pairing and (tile, batch column, row): at a level of m nodes, nodes 2j and
 // 2j+1 share word j, each setting its half with one atomic OR (the fp32 bits
 // inverted, so that an empty half reads 0; -0.0 and +0.0 stay distinct); an
-// odd last one passes up unpaired.  The one that finds the other half already
-// there adds left + right, clears the word and goes on to the next level;
-// the last one rounds once and stores y.  Which workgroup arrives first does
-// not change any sum, so repeated launches give identical bits, and every
-// word is zero again when the launch has finished.
+// odd last node passes up unpaired.  The one that finds the other half
+// already there adds left + right, clears the word and goes on to the next
+// level; the last one rounds once and stores y.  Which workgroup arrives
+// first does not change any sum, so repeated launches give identical bits,
+// and every word is zero again when the launch has finished.
+// Without helpers the tree spans the split's leaves, words from t * stride
+// (stride = split - 1).  With e > 0 helpers (an outlier plan; stride =
+// kMaxSplit - 1) the owners' leaves [0, split) and the helpers' [split,
+// split + e) first form a tree each, (split - 1) and (e - 1) words, and the
+// two roots meet in one more word: helpers hold no code stream and finish
+// early, so an owner that arrives last climbs its own tree and one word.
+template <int B>
+__device__ __forceinline__ bool climb(const KernelArgs &a, int t, int stride, int b, int lane, float &v, int i, int m,
+                                      int base)
+{
+    while (m > 1) {
+        if ((m & 1) && i == m - 1) { // unpaired: passes up as it is
+            i >>= 1;
+            base += m >> 1;
+            m = (m + 1) >> 1;
+            continue;
+        }
+        unsigned long long *w = a.slots + (((int64_t)t * stride + base + (i >> 1)) * B + b) * 64 + lane;
+        const uint32_t enc = ~__float_as_uint(v);
+        const unsigned long long mine = (i & 1) ? (unsigned long long)enc << 32 : (unsigned long long)enc;
+        const unsigned long long old = __hip_atomic_fetch_or(w, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t other = (i & 1) ? (uint32_t)old : (uint32_t)(old >> 32);
+        if (other == 0) return false; // the partner has not arrived: it goes on
+        const float o = __uint_as_float(~other);
+        v = (i & 1) ? o + v : v + o; // left + right
+        __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        i >>= 1;
+        base += m >> 1;
+        m = (m + 1) >> 1;
+    }
+    return true;
+}
+
 template <int B, bool ADDY>
-__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int s, int lane, const float *tot, int count)
+__device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int s, int lane, const float *tot, int split,
+                                            int e, int stride)
 {
     const int row = t * 64 + lane;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         float v = tot[b];
-        int i = s, m = count, base = 0;
-        bool last = true;
-        while (m > 1) {
-            if ((m & 1) && i == m - 1) { // unpaired: passes up as it is
-                i >>= 1;
-                base += m >> 1;
-                m = (m + 1) >> 1;
-                continue;
-            }
-            unsigned long long *w = a.slots + (((int64_t)t * (count - 1) + base + (i >> 1)) * B + b) * 64 + lane;
-            const uint32_t enc = ~__float_as_uint(v);
-            const unsigned long long mine = (i & 1) ? (unsigned long long)enc << 32 : (unsigned long long)enc;
-            const unsigned long long old = __hip_atomic_fetch_or(w, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t other = (i & 1) ? (uint32_t)old : (uint32_t)(old >> 32);
-            if (other == 0) { // the partner has not arrived: it goes on
-                last = false;
-                break;
-            }
-            const float o = __uint_as_float(~other);
-            v = (i & 1) ? o + v : v + o; // left + right
-            __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            i >>= 1;
-            base += m >> 1;
-            m = (m + 1) >> 1;
-        }
+        bool last;
+        if (e == 0)
+            last = climb<B>(a, t, stride, b, lane, v, s, split, 0);
+        else if (s < split)
+            last = climb<B>(a, t, stride, b, lane, v, s, split, 0) &&
+                   climb<B>(a, t, stride, b, lane, v, 0, 2, split + e - 2);
+        else
+            last = climb<B>(a, t, stride, b, lane, v, s - split, e, split - 1) &&
+                   climb<B>(a, t, stride, b, lane, v, 1, 2, split + e - 2);
         if (last && row < a.rows) {
             if constexpr (ADDY) v += f16_to_f32(a.y[(int64_t)b * a.ldy + row]);
             a.y[(int64_t)b * a.ldy + row] = f32_to_f16_rne(v);
@@ -763,13 +781,78 @@ __device__ __forceinline__ void finish_rows(const KernelArgs &a, int t, int s, i
 // the first ring of code loads, then the first round of nonzeros.  Every dense step issues one group of loads
 // (placeholders past the wave's last group), so the wait before each group's
 // math lets exactly D-1 groups stay in flight.
+// A helper workgroup of an outlier plan: share s of tile t's nonzeros (of
+// count * W even shares, as the tile's owners cut them), nothing else -- no
+// pair table, no code loads, whose queue it would otherwise wait behind --
+// then the wave reduction and leaf s of the tile's combine.
+// red: LDS for the reduction (W * B * 64 floats); xs: LDS for x when staged.
+template <int B, bool ADDY>
+__device__ __forceinline__ void helper_body(const KernelArgs &a, int t, int s, int count, float *red, uint32_t *xs)
+{
+    constexpr int NC = 1;
+    constexpr int R = B <= 2 ? 8 : (B <= 8 ? 4 : 2); // chunks per round: their gathers stay in registers
+    const int nt = blockDim.x;
+    const int W = nt >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row0 = t * 64;
+    const int rp_lo = a.row_ptr[min(row0 + lane, a.rows)];
+    const int rp_hi = a.row_ptr[min(row0 + lane + 1, a.rows)];
+    const int nz0 = __builtin_amdgcn_readfirstlane(rp_lo);
+    const int nz1 = __builtin_amdgcn_readlane(rp_hi, 63);
+    const uint32_t len = (uint32_t)(nz1 - nz0);
+    const uint32_t parts = (uint32_t)(count * W), part = (uint32_t)(w * count + s);
+    const uint32_t per = len / parts, extra = len - per * parts;
+    const int v0 = nz0 + (int)(part * per + min(part, extra));
+    const int v1 = v0 + (int)(per + (part < extra ? 1u : 0u));
+    if (a.x_lds) { // uniform: all of x into LDS
+        const int nxq = B * (a.cols >> 3);
+        for (int i = threadIdx.x; i < nxq; i += nt) ((u32x4 *)xs)[i] = ((const u32x4 *)a.x)[i];
+        lds_barrier();
+    }
+    const uint16_t *xl = (const uint16_t *)xs;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    SparseRound<R> cv;
+    for (int base = v0; base < v1; base += 64 * R) {
+        sparse_round_load(cv, a, base, v1, lane);
+        uint16_t xg[R][B];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (base + 64 * k < v1) {
+                if (a.x_lds)
+                    sparse_gather<B, true>(cv.col[k], a, xl, xg[k]);
+                else if (B >= kXtBatch && a.xt)
+                    sparse_gather_t<B>(cv.col[k], a.xt, xg[k]);
+                else
+                    sparse_gather<B, false>(cv.col[k], a, xl, xg[k]);
+            }
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (base + 64 * k < v1) sparse_scan<B, NC>(cv.val[k], xg[k], base + 64 * k, v1, lane, rp_lo, rp_hi, acc);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) red[(w * B + b) * 64 + lane] = acc[b];
+    lds_barrier();
+    if (w != 0) return;
+    float tot[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float v = 0.f;
+        for (int k = 0; k < W; ++k) v += red[(k * B + b) * 64 + lane];
+        tot[b] = v;
+    }
+    finish_rows<B, ADDY>(a, t, s, lane, tot, a.split, count - a.split, kMaxSplit - 1);
+}
+
 // Every argument (and the workgroup size) into registers at once: one round
 // of scalar loads at the start instead of one per first use.
 __device__ __forceinline__ void load_args_now(const KernelArgs &a)
 {
     asm volatile("" ::"s"(a.packed), "s"(a.lut), "s"(a.row_ptr), "s"(a.col), "s"(a.val), "s"(a.x), "s"(a.y),
                  "s"(a.slots), "s"(a.rows), "s"(a.ldy), "s"(a.cols), "s"(a.tiles), "s"(a.groups), "s"(a.split), "s"(a.gps),
-                 "s"(a.x_lds), "s"(a.xt), "s"(a.sparse_naive), "s"(blockDim.x));
+                 "s"(a.x_lds), "s"(a.xt), "s"(a.sparse_naive), "s"(a.plan), "s"(a.helpers), "s"(blockDim.x));
 }
 
 template <int BITS, int B, int MODE, bool MF>
@@ -790,7 +873,28 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     const int W = nt >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int t = bid / a.split, s = bid - t * a.split;
+    // Workgroups [0, helpers) of a planned launch are helpers: helper h takes
+    // leaf split + e of tile t's combine (plan entry (t << 4) | e) and only
+    // outliers; the rest own (tile, column range) pairs as without a plan.
+    // count: the tile's partial sums (its owners and helpers).
+    typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr; // read-only: scalar loads
+    const bool helper = bid < a.helpers;
+    int t, s;
+    if (helper) {
+        const int e = ((const_i32_ptr)a.plan)[1 + a.tiles + bid];
+        t = e >> 4;
+        s = a.split + (e & 15);
+    } else {
+        t = (bid - a.helpers) / a.split;
+        s = bid - a.helpers - t * a.split;
+    }
+    const int count = a.helpers > 0 ? a.split + ((const_i32_ptr)a.plan)[1 + t] : a.split;
+    if constexpr (SPARSE) {
+        if (helper) { // uniform over the workgroup
+            helper_body<B, ADDY>(a, t, s, count, (float *)tab, dyn);
+            return;
+        }
+    }
     const int row0 = t * 64;
     const uint32_t lane4 = (uint32_t)lane << 2;
 
@@ -839,7 +943,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     //       a queue of streaming code loads delays the table's loads)
     const int gb = s * a.gps;
     const int ge = min(gb + a.gps, a.groups);
-    const int cnt = DENSE ? max(0, (ge - gb - w + W - 1) / W) : 0; // this wave's groups
+    const int cnt = DENSE && !helper ? max(0, (ge - gb - w + W - 1) / W) : 0; // this wave's groups
     GroupRegs<BITS, B, MF> ring[DENSE ? D : 1];
     auto issue_ring = [&]() {
         if constexpr (DENSE) {
@@ -862,13 +966,12 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     if constexpr (SPARSE) {
         // the tile's ends, as uniform (scalar) loads: waiting for them does
         // not wait for the vector loads in flight
-        typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr; // read-only: scalar loads
         const const_i32_ptr rptr = (const_i32_ptr)a.row_ptr;
         nz0 = rptr[row0];
         const int nz1 = rptr[min(row0 + 64, a.rows)];
         // share part of `parts` even shares: the first len % parts get one more
         const uint32_t len = (uint32_t)(nz1 - nz0);
-        const uint32_t parts = (uint32_t)(a.split * W), part = (uint32_t)(w * a.split + s);
+        const uint32_t parts = (uint32_t)(count * W), part = (uint32_t)(w * count + s);
         const uint32_t per = len / parts, extra = len - per * parts;
         v0 = nz0 + (int)(part * per + min(part, extra));
         v1 = v0 + (int)(per + (part < extra ? 1u : 0u));
@@ -1018,7 +1121,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         for (int k = 0; k < W; ++k) v += red[(k * B + b) * 64 + lane];
         tot[b] = v;
     }
-    finish_rows<B, ADDY>(a, t, s, lane, tot, a.split);
+    finish_rows<B, ADDY>(a, t, s, lane, tot, a.split, count - a.split, a.helpers > 0 ? kMaxSplit - 1 : count - 1);
 }
 
 template <int BITS, int B, int MODE, bool MF>
@@ -1038,7 +1141,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(Grou
 {
     const KernelArgs &a = g.item[blockIdx.y];
     load_args_now(a);
-    if ((int)blockIdx.x >= a.tiles * a.split) return;
+    if ((int)blockIdx.x >= a.tiles * a.split + a.helpers) return;
     product_body<BITS, B, MODE, MF>(a, blockIdx.x);
 }
 
@@ -1068,7 +1171,7 @@ hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t st
     raise_lds_limit((const void *)kern, attr_devices,
                     kLdsBudget - (MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4));
     if (ls.waves < 1 || ls.waves > kMaxWaves) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(a.tiles * a.split)), block((unsigned)(64 * ls.waves));
+    const dim3 grid((unsigned)(a.tiles * a.split + a.helpers)), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, a);
     return hipGetLastError();
 }

@@ -14,7 +14,8 @@ constexpr int kGroupCols = 256;   // codes per group
 constexpr int kMaxBatch = 16;
 constexpr int kMaxDotBatch = 8;   // the v_dot2c form is built up to this batch; above it only the matrix cores
 constexpr int kMaxWaves = 16;     // waves per workgroup
-constexpr int kMaxSplit = 16;     // workgroups sharing one row tile
+constexpr int kMaxSplit = 16;     // workgroups sharing one row tile (the owners and any helpers)
+constexpr int kMaxHelpers = 8;    // helpers one row tile may get from an outlier plan
 constexpr int kTableBytes = 256 * 64 * 4;           // pair table: 256 entries x 64 lanes x half2
 constexpr int kLdsBudget = 160 * 1024;              // LDS per compute unit on gfx950
 constexpr int kSparseShare = 512; // outlier nonzeros per wave the outlier-only kernel aims for
@@ -38,6 +39,8 @@ struct KernelArgs {
     int x_lds;                // 1: all of x staged in LDS for the outlier gathers
     const uint16_t *xt;       // else, batch >= kXtBatch: x transposed, [cols][xt_pad(batch)] fp16 (or null)
     int sparse_naive;         // 1 (ablation): one lane per row walks its own nonzeros, no balancing
+    const int32_t *plan;      // with helpers > 0: per-tile helper counts at plan[1 + t], then the helpers
+    int helpers;              // workgroups that only take shares of a heavy tile's nonzeros (grid's first)
 };
 
 // Independent products run by one launch (same bits and batch).

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
@@ -192,6 +192,73 @@ def test_group_argument_errors(lib, nwpkg):
     # split workgroups need the workspace: one tile of 8192 columns is split
     assert group(lib, nwpkg, n=1, cols=8192, ws=None) == 8
     assert group(lib, nwpkg, n=1, cols=8192, wsb=16) == 8
+    # outlier plans: helpers need the plan, 4-byte aligned, at most 8 per row tile
+    assert group(lib, nwpkg, plan=None, plan_helpers=1) == 1
+    assert group(lib, nwpkg, plan=0x100002, plan_helpers=1) == 5
+    assert group(lib, nwpkg, plan=A16.value, plan_helpers=9) == 3      # one tile of 64 rows
+    assert group(lib, nwpkg, plan=A16.value, plan_helpers=-1) == 3
+    # a planned tile combines up to 16 partial sums: 15 words per output are needed
+    assert group(lib, nwpkg, n=1, plan=A16.value, plan_helpers=1, wsb=15 * 64 * 8 - 1) == 8
+
+
+def _plan(nwpkg, counts, rows=None):
+    """Row pointers with `counts` nonzeros per row (the rest empty), and their outlier plan."""
+    counts = list(counts)
+    rows = rows or len(counts)
+    counts += [0] * (rows - len(counts))
+    rp = [0]
+    for c in counts:
+        rp.append(rp[-1] + c)
+    return nwpkg.outlier_plan(rp)
+
+
+def test_outlier_plan_rule(nwpkg):
+    """A tile above twice the average tile's nonzeros gets ceil(n / q) - 1 helpers (at most 8),
+    q = 2 ceil(nnz / tiles); entries (t << 4) | e follow in tile order."""
+    # 4 tiles of 64 rows holding 10, 10, 10 and 370 nonzeros: q = 2 * 100 = 200, the last tile gets 1
+    counts = [0] * 256
+    for t, n in enumerate((10, 10, 10, 370)):
+        counts[64 * t] = n
+    plan = _plan(nwpkg, counts)
+    assert list(plan) == [1, 0, 0, 0, 1, (3 << 4) | 0]
+    # a 5000-nonzero tile among 7 of 100: q = 2 * ceil(5700 / 8) = 1426, ceil(5000 / 1426) - 1 = 3
+    counts = [0] * 512
+    for t in range(8):
+        counts[64 * t + 5] = 100 if t != 2 else 5000
+    plan = _plan(nwpkg, counts)
+    assert list(plan[:9]) == [3, 0, 0, 3, 0, 0, 0, 0, 0]
+    assert list(plan[9:]) == [(2 << 4) | 0, (2 << 4) | 1, (2 << 4) | 2]
+    # capped at 8 helpers per tile; a ragged last tile (2 rows) counts as a tile: 100 tiles, 99 of 10
+    # nonzeros and the last of 100000, q = 2 * ceil(100990 / 100) = 2020, ceil(100000 / 2020) - 1 = 49 -> 8
+    counts = [0] * (64 * 99 + 2)
+    for t in range(99):
+        counts[64 * t] = 10
+    counts[-1] = 100000
+    plan = _plan(nwpkg, counts)
+    assert plan[0] == 8 and not plan[1:100].any() and plan[100] == 8
+    assert list(plan[101:]) == [(99 << 4) | e for e in range(8)]
+    # uniform rows and an empty CSR get no helpers
+    assert list(_plan(nwpkg, [3] * 1000)[:1]) == [0]
+    assert list(_plan(nwpkg, [0] * 100)) == [0, 0, 0]
+
+
+def test_outlier_plan_errors(lib, nwpkg):
+    f = lib.sqllm_outlier_plan
+    rp = (ctypes.c_int32 * 3)(0, 2, 5)
+    buf = (ctypes.c_int32 * 16)()
+    assert lib.sqllm_outlier_plan_len(2) == 1 + 1 + 8
+    assert lib.sqllm_outlier_plan_len(0) == 0
+    assert f(rp, 2, buf, 16) == 2
+    assert f(None, 2, buf, 16) == 0
+    assert f(rp, 2, None, 16) == 0
+    assert f(rp, 2, buf, 9) == 0                      # below sqllm_outlier_plan_len
+    assert f(rp, 0, buf, 16) == 0
+    bad = (ctypes.c_int32 * 3)(1, 2, 5)               # must start at 0
+    assert f(bad, 2, buf, 16) == 0
+    bad = (ctypes.c_int32 * 3)(0, 5, 2)               # and never decrease
+    assert f(bad, 2, buf, 16) == 0
+    with pytest.raises(ValueError):
+        nwpkg.outlier_plan([0, 3, 1])
 
 
 def test_group_workspace_bytes(lib, nwpkg):

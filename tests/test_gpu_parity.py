@@ -14,7 +14,7 @@ import oracle
 from seeds import stable_seed
 import synth
 from gpu_util import DevMatrix, assert_close, dev_to_u16, nw, step, u16_to_dev
-from test_oracle_pins import _make_case, pack_from_definition
+from test_oracle_pins import _make_case, _rand_f16, pack_from_definition
 
 pytestmark = pytest.mark.gpu
 
@@ -524,6 +524,109 @@ def test_group_matches_oracle(bits, batch):
     for (codes, lut, x, rp, col, val), y, shape in zip(cases, ys, GROUP_CASES):
         y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
         assert_close(y, y_ref, scale, TOL, f"group item {shape}")
+
+
+def _plan_dev(row_ptr):
+    plan = nw().outlier_plan(row_ptr)
+    return torch.from_numpy(plan).cuda(), int(plan[0])
+
+
+def _heavy_tiles_case(rng, rows, cols, bits, batch, heavy_rows):
+    """Sparse rows (1%) plus a few fully dense rows, so that their tiles hold
+    far more nonzeros than the rest."""
+    codes = rng.integers(0, 1 << bits, (rows, cols)).astype(np.uint8)
+    lut = _rand_f16(rng, (rows, 1 << bits), 0.02)
+    x = _rand_f16(rng, (batch, cols), 1.0)
+    mask = rng.random((rows, cols)) < 0.01
+    mask[list(heavy_rows)] = True
+    r, c = np.nonzero(mask)
+    rp = np.zeros(rows + 1, np.int32)
+    np.add.at(rp, r + 1, 1)
+    rp = np.cumsum(rp).astype(np.int32)
+    return codes, lut, x, rp, c.astype(np.uint16), _rand_f16(rng, (r.size,), 0.5)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("batch", [1, 3, 6, 16])
+def test_outlier_plan_heavy_tiles(bits, batch):
+    """Tiles with fully dense rows get helper workgroups from the outlier
+    plan: every output within tolerance of the oracle (the ragged last tile
+    heavy too), repeated calls bit-identical, the workspace zero again."""
+    rng = np.random.default_rng(stable_seed("plan", bits, batch))
+    rows, cols = 4000, 4096
+    codes, lut, x, rp, col, val = _heavy_tiles_case(rng, rows, cols, bits, batch, (70, 71, 72, 600, 3998, 3999))
+    plan, h = _plan_dev(rp)
+    assert h > 0
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    ws = torch.zeros(nw().workspace_bytes(rows, cols, batch), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        y = torch.full((batch, rows), float("nan"), dtype=torch.float16, device="cuda")
+        step(f"planned heavy tiles bits {bits} batch {batch} helpers {h}")
+        nw().dense_sparse_gemv_group([dict(packed=d.packed, lut=d.lut, row_ptr=d.row_ptr, col=d.col, val=d.val,
+                                           x=d.x, y=y, plan=plan)], bits, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(dev_to_u16(y))
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    ok, worst = oracle.within_tolerance(outs[0], y_ref, scale, TOL)
+    assert ok, f"max normalised error {worst:.3e}"
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    assert int(ws.view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("index", [0, 4, 6])
+@pytest.mark.parametrize("batch", [1, 6])
+def test_outlier_plan_13b_zipf(index, batch):
+    """The 13B layer's products with Zipf rows (the skewed workload), planned:
+    every row against the oracle, bit-identical repeats."""
+    s = synth.workload(3)[index]
+    spec = synth.MatrixSpec(s.name, s.rows, s.cols, s.bits, batch, s.density_bp, s.zipf)
+    m = synth.make_matrix(spec, seed=0, workload=3, index=index)
+    plan, h = _plan_dev(m.row_ptr)
+    assert h > 0
+    d = DevMatrix.from_synth(m)
+    step(f"planned 13B {spec.name} batch {batch} helpers {h}")
+    item = dict(packed=d.packed, lut=d.lut, row_ptr=d.row_ptr, col=d.col, val=d.val, x=d.x, plan=plan,
+                plan_helpers=h)
+    outs = []
+    for _ in range(2):
+        y = torch.full((batch, spec.rows), float("nan"), dtype=torch.float16, device="cuda")
+        nw().dense_sparse_gemv_group([dict(item, y=y)], spec.bits)
+        torch.cuda.synchronize()
+        outs.append(dev_to_u16(y))
+    assert np.array_equal(outs[0], outs[1])
+    y_ref, scale = oracle.dense_sparse_gemv(m.codes, m.lut, spec.bits, m.row_ptr, m.col, m.val, m.x)
+    ok, worst = oracle.within_tolerance(outs[0], y_ref, scale, TOL)
+    assert ok, f"max normalised error {worst:.3e}"
+
+
+@pytest.mark.parametrize("split", [0, 1, 3, 8])
+def test_outlier_plan_in_mixed_groups(split):
+    """A group mixing a planned product, an unplanned one, a plan without
+    helpers and a product without outliers, at default and forced splits
+    (owners plus helpers up to 16 partial sums per tile)."""
+    rng = np.random.default_rng(stable_seed("plan-mixed", split))
+    bits, batch = 3, 2
+    cases = [_heavy_tiles_case(rng, 300, 2048, bits, batch, (5, 6, 290)),
+             _make_case(rng, 193, 4096, bits, batch, "5pct"),
+             _make_case(rng, 130, 1024, bits, batch, "5pct"),
+             _make_case(rng, 64, 256, bits, batch, "none")]
+    mats = [DevMatrix(*c[:2], bits, *c[3:], c[2]) for c in cases]
+    ys = [torch.full((batch, d.rows), float("nan"), dtype=torch.float16, device="cuda") for d in mats]
+    items = _items(mats, ys)
+    items[0]["plan"], h0 = _plan_dev(cases[0][3])
+    items[2]["plan"], h2 = _plan_dev(cases[2][3])
+    assert h0 > 0 and h2 == 0
+    step(f"planned mixed group split {split} helpers {h0}")
+    try:
+        nw().set_tuning(split=split)
+        nw().dense_sparse_gemv_group(items, bits)
+        torch.cuda.synchronize()
+    finally:
+        nw().set_tuning()
+    for (codes, lut, x, rp, col, val), y in zip(cases, ys):
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+        assert_close(y, y_ref, scale, TOL, f"mixed planned group, split {split}")
 
 
 @pytest.mark.parametrize("batch", [1, 5])
