@@ -58,13 +58,15 @@ def parse():
                    help="skip the one-call-per-product pass, so that a profiler sees only the group launches")
     p.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: min(16, cpus))")
     p.add_argument("--no-per-matrix", action="store_true",
-                   help="skip the cold single-matrix timings of the 7B, 7B-MLP, 13B and 65B shapes at batch 1")
-    p.add_argument("--ablation", choices=("outliers", "batch", "offline", "configs"), default=None,
+                   help="skip the cold single-matrix timings of the 7B, 7B-MLP, 13B and 65B shapes at batch 1 and the "
+                        "launch-structure ceiling (the stream's launches as plain reads)")
+    p.add_argument("--ablation", choices=("outliers", "batch", "offline", "configs", "ceiling"), default=None,
                    help="outliers: time each product of the 13B (skewed rows) and 65B (uniform) workloads "
                         "dense-only, with balanced outliers, with one-thread-per-row outliers, and stream-ordered "
                         "(one JSON line of its own); batch: the 65B shapes at batch 1, 2, 4, 8, 16 in both dense forms; offline: the "
                         "dense-and-sparse split and weighted k-means of one 65B layer, with the oracle on a sample; configs: "
-                        "every matrix of the 7B, 7B-MLP, 13B and 65B single-matrix workloads, cold and warm")
+                        "every matrix of the 7B, 7B-MLP, 13B and 65B single-matrix workloads, cold and warm; ceiling: the "
+                        "stream's launches as plain reads of the same bytes with no arithmetic")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="after the timing, copy BYTES device-to-device once (a reference for counter runs)")
     return p.parse_args()
@@ -719,6 +721,75 @@ def offline_ablation(args) -> None:
     print(json.dumps(out), flush=True)
 
 
+def launch_ceiling(args, reps: int) -> dict:
+    """The launch structure's ceiling: one step of the stream as the same 320
+    dependent launches (per layer (q,k,v), (o), (gate,up), (down)), each a
+    plain read of exactly that launch's algorithmic bytes (rounded down to
+    1 KiB) with no decode or arithmetic (sqllm_test_stream_read), captured in
+    one HIP graph; and the same bytes as one launch."""
+    import torch
+
+    import non_uniform_weight_amd as nw
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    specs = synth.workload(5, bits=args.bits, density_bp=args.density_bp)[:7 * args.layers]
+    sizes = []
+    for l0 in range(0, len(specs), 7):
+        for lv in WeightStream.LEVELS:
+            b = sum(nw.algorithmic_bytes(specs[l0 + i].rows, specs[l0 + i].cols, specs[l0 + i].bits,
+                                         specs[l0 + i].nnz, 1) for i in lv)
+            sizes.append(b // 1024 * 1024)
+    total = sum(sizes)
+    buf = torch.ones(total, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    lib, h = nw.library(), vp_stream(stream)
+    base = buf.data_ptr()
+
+    def step_fn():
+        off = 0
+        for n in sizes:
+            st = lib.sqllm_test_stream_read(base + off, n, sink.data_ptr(), h)
+            if st != 0:
+                raise RuntimeError(f"sqllm_test_stream_read failed with status {st}")
+            off += n
+
+    def timed(fn, reps):
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step_fn()
+    ms_graph = timed(g.replay, reps)
+    ms_one = timed(lambda: lib.sqllm_test_stream_read(base, total, sink.data_ptr(), h), reps)
+    del g, buf
+    torch.cuda.empty_cache()
+    out = {"launches_per_step": len(sizes), "bytes_per_step": total,
+           "launches_as_reads": {"ms_per_step": round(ms_graph, 4), "GB_per_s": round(total / ms_graph / 1e6, 1),
+                                 "frac": round(total / ms_graph / 1e6 / HBM_PEAK_GBS, 4),
+                                 "us_per_launch": round(ms_graph * 1e3 / len(sizes), 3)},
+           "one_read": {"ms": round(ms_one, 4), "GB_per_s": round(total / ms_one / 1e6, 1),
+                        "frac": round(total / ms_one / 1e6 / HBM_PEAK_GBS, 4)}}
+    log(f"ceiling: {len(sizes)} reads {ms_graph:.3f} ms ({total / ms_graph / 1e6:.0f} GB/s), one read {ms_one:.3f} ms "
+        f"({total / ms_one / 1e6:.0f} GB/s)")
+    return out
+
+
+def ceiling_ablation(args) -> None:
+    print(json.dumps(dict(ablation="ceiling", **launch_ceiling(args, args.steps))), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -736,6 +807,9 @@ def main():
         return
     if args.ablation == "configs":
         config_table(args)
+        return
+    if args.ablation == "ceiling":
+        ceiling_ablation(args)
         return
     import torch
 
@@ -806,6 +880,7 @@ def main():
     del ws
     torch.cuda.empty_cache()
     matrices = None if args.no_per_matrix else per_matrix(args.seed, stream)
+    ceiling = None if args.no_per_matrix else launch_ceiling(args, 20)
     cpu = None
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
@@ -855,6 +930,9 @@ def main():
             "algorithmic_bytes_per_launch": round(avg_bytes),
         },
         "per_matrix": matrices,
+        # the same launches as plain reads of the same bytes, no arithmetic: what any kernel could reach with
+        # this launch structure
+        "launch_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -404,6 +404,21 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,
                                uint16_t *w, hipStream_t stream);
 
+/*
+ * sqllm_test_stream_read -- test-only reference for the HBM roofline (§3.4
+ * "The Memory-Bound Analysis": the product is bound by the bytes it loads):
+ * reads `bytes` of device memory at `src` (16-byte aligned, a multiple of
+ * 1024) once with wide non-temporal loads, 1024 workgroups of 4 waves each
+ * streaming a contiguous range with 8 loads in flight, no arithmetic beyond
+ * an XOR of the 32-bit words.  sink: device uint32 [4096], entry w = the XOR
+ * of the words wave w read (the XOR of all entries is that of the whole
+ * range).  Timed as one launch per product it gives the rate a launch with
+ * no decode could reach at the same launch count.
+ * Async on `stream`; SQLLM_ERR_SHAPE for bytes not a positive multiple of
+ * 1024, SQLLM_ERR_NULL / SQLLM_ERR_ALIGN for src or sink.
+ */
+sqllm_status sqllm_test_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

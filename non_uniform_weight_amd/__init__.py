@@ -81,6 +81,8 @@ _lib.sqllm_test_tuning.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 _lib.sqllm_test_launch_plan.restype = _i32
 _lib.sqllm_test_launch_plan.argtypes = [_i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                         _i32, _sz, ctypes.POINTER(_i32)]
+_lib.sqllm_test_stream_read.restype = _i32
+_lib.sqllm_test_stream_read.argtypes = [_vp, _sz, _vp, _vp]
 _lib.sqllm_test_decode.restype = _i32
 _lib.sqllm_test_decode.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
 
@@ -89,7 +91,7 @@ EXPORTS = ("sqllm_status_string", "sqllm_packed_bytes", "sqllm_workspace_bytes",
            "sqllm_dense_sparse_gemv_group", "sqllm_quantize_workspace_bytes", "sqllm_outlier_thresholds",
            "sqllm_outlier_extract", "sqllm_kmeans_lut", "sqllm_test_unpack", "sqllm_test_decode", "sqllm_test_tuning",
            "sqllm_test_launch_plan", "sqllm_dense_sparse_gemv_noalloc", "sqllm_outlier_plan_len",
-           "sqllm_outlier_plan")
+           "sqllm_outlier_plan", "sqllm_test_stream_read")
 MAX_GROUP = 8
 
 SQLLM_OK = 0
@@ -288,6 +290,15 @@ def group_products(items, bits: int):
         arr[k] = Product(_dev(it["packed"], "packed", torch.uint8), _dev(it["lut"], "lut", torch.float16), rp, ci, cv,
                          nnz, rows, cols, _dev(x, "x", torch.float16), _dev(y, "y", torch.float16), pp, ph)
     return arr, batch
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, stream=None) -> None:
+    """Test-only: read nbytes (default all) of src once; sink (int32 [4096] on the device) receives each
+    wave's XOR of the 32-bit words it read."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if not (src.is_cuda and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= 4096):
+        raise ValueError("stream_read: device src and an int32 device sink of 4096 entries expected")
+    _check(_lib.sqllm_test_stream_read(src.data_ptr(), n, sink.data_ptr(), _stream(stream)), "sqllm_test_stream_read")
 
 
 def group_workspace_bytes(items, bits: int) -> int:

@@ -520,6 +520,14 @@ size_t sqllm_group_workspace_bytes(const sqllm_product *items, int n, int batch)
     return total;
 }
 
+sqllm_status sqllm_test_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (!src || !sink) return SQLLM_ERR_NULL;
+    if (bytes == 0 || bytes % 1024 != 0) return SQLLM_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return SQLLM_ERR_ALIGN;
+    return launch_stream_read(src, bytes, sink, stream) == hipSuccess ? SQLLM_OK : SQLLM_ERR_HIP;
+}
+
 size_t sqllm_outlier_plan_len(int64_t rows)
 {
     if (rows < 1 || rows > (int64_t)1 << 30) return 0;

@@ -115,6 +115,8 @@ struct XtJobs {
     uint16_t *xt[kMaxGroup];
     int cols[kMaxGroup];
 };
+constexpr int kStreamReadWaves = 4096; // waves of the reference read stream: one sink slot each
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_xt_write(const XtJobs &j, int batch, hipStream_t stream);
 hipError_t launch_xt_clear(const XtJobs &j, int batch, hipStream_t stream);
 

@@ -279,6 +279,51 @@ hipError_t launch_xt_clear(const XtJobs &j, int batch, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Reference read stream (test-only): the range's pieces of 1 KiB are cut
+// into even contiguous shares, one per wave (the first pieces % waves
+// shares one piece longer; lane l reads bytes l*16 .. l*16+15 of each
+// piece), D loads in flight, and every word is folded
+// into an XOR, stored to the wave's own sink slot (one atomic per wave on a
+// shared word would serialise: ~37 ns each, 151 us per launch).  Every step issues D
+// loads (indices past the range clamped to its last piece, their words
+// masked out), so the compiler's wait counts stay exact.
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4 *src, int64_t pieces, uint32_t *sink)
+{
+    constexpr int D = 8;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t per = pieces / nwaves, rem = pieces - per * nwaves;
+    const int64_t p0 = wid * per + min(wid, rem);
+    const int64_t p1 = p0 + per + (wid < rem ? 1 : 0);
+    uint32_t acc = 0;
+    if (p0 < p1) {
+        const u32x4 *base = src + lane;
+        u32x4 r[D];
+#pragma unroll
+        for (int k = 0; k < D; ++k) r[k] = __builtin_nontemporal_load(base + min(p0 + k, p1 - 1) * 64);
+        for (int64_t j = p0; j < p1; j += D) {
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                const uint32_t v = r[k].x ^ r[k].y ^ r[k].z ^ r[k].w;
+                acc ^= j + k < p1 ? v : 0u;
+                r[k] = __builtin_nontemporal_load(base + min(j + k + D, p1 - 1) * 64);
+            }
+        }
+    }
+    // fold the wave's lanes into its slot
+    for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    if (lane == 0) sink[wid] = acc;
+}
+
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    const int64_t pieces = (int64_t)(bytes / 1024);
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamReadWaves / 4), dim3(256), 0, stream, (const u32x4 *)src,
+                       pieces, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t *codes, int rows, int cols, int bits, void *packed, int *bad, hipStream_t stream)
 {
     const int groups = cols / 256, tiles = (rows + 63) / 64;

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib, nwpkg):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(nwpkg.EXPORTS)
@@ -240,6 +240,16 @@ def test_outlier_plan_rule(nwpkg):
     # uniform rows and an empty CSR get no helpers
     assert list(_plan(nwpkg, [3] * 1000)[:1]) == [0]
     assert list(_plan(nwpkg, [0] * 100)) == [0, 0, 0]
+
+
+def test_stream_read_argument_errors(lib):
+    f = lib.sqllm_test_stream_read
+    assert f(None, 1024, B16, None) == 1
+    assert f(A16, 1024, None, None) == 1
+    assert f(A16, 0, B16, None) == 3
+    assert f(A16, 1000, B16, None) == 3                 # whole KiB only
+    assert f(P(0x100008), 1024, B16, None) == 5
+    assert f(A16, 1024, P(0x200002), None) == 5
 
 
 def test_outlier_plan_errors(lib, nwpkg):

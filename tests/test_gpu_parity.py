@@ -303,6 +303,22 @@ def test_two_streams_default_workspaces():
             assert_close(y, y_ref, scale, TOL, f"stream {k}")
 
 
+@pytest.mark.parametrize("kib", [1, 5, 4095, 4096 * 9 + 7])
+def test_stream_read_reads_every_word_once(kib):
+    """The reference read stream behind the ceiling measurement reads each
+    32-bit word exactly once: its XOR equals numpy's (ragged ranges, fewer
+    pieces than waves, a tail on the last wave)."""
+    rng = np.random.default_rng(kib)
+    words = rng.integers(0, 2 ** 32, kib * 256, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.full((4096,), -1, dtype=torch.int32, device="cuda")
+    step(f"stream read {kib} KiB")
+    nw().stream_read(src, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    assert int(np.bitwise_xor.reduce(got)) == int(np.bitwise_xor.reduce(words))
+
+
 def test_permuted_table_with_remapped_codes():
     """Permuting a row's table entries together with its codes leaves y unchanged."""
     step("lut permutation invariance")
