@@ -857,7 +857,9 @@ def main():
     if args.launch == "level":
         ms = time_mode(ws.step_grouped)
         n_launches = len(ws.groups)
-        kernel = f"dense_sparse_group_kernel<{args.bits},1,fused,matrix>"
+        # (q,k,v) and (gate,up) run dense_sparse_group_kernel, the one-product levels (o) and (down)
+        # dense_sparse_kernel: one kernel body, its arguments from a per-product table or passed directly
+        kernel = f"dense_sparse{{,_group}}_kernel<{args.bits},1,fused,matrix>"
         log(f"group launches, {mode}: {ms:.3f} ms/step ({n_launches} launches)")
     else:
         # 22016x8192 (344 row tiles) runs as two row slices in one group launch
