@@ -924,3 +924,40 @@ def test_unbalanced_outlier_form_skewed_workload_rows():
         _check_matrix(m, np.arange(0, spec.rows, 7))
     finally:
         nw().set_tuning()
+
+
+# ------------------------------------------------------------ the widest rows
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("batch", [1, 9])
+def test_maximum_columns(bits, batch):
+    """cols = 65536, the most that 16-bit column indices address: x is then
+    too wide to stage in LDS, so the outliers gather it from memory (from
+    batch 5 on, from the transposed copy).  Nonzeros sit in the first and the
+    last column, and the rows end in a ragged tile.  The fused, dense-only,
+    stream-ordered, group and allocation-free calls all match the oracle."""
+    rows, cols = 65, 65536
+    rng = np.random.default_rng(stable_seed("maxcols", bits, batch))
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, bits, batch, "5pct")
+    col = col.copy()
+    assert rp[1] > rp[0] and rp[rows] > rp[rows - 1]
+    col[rp[0]] = cols - 1      # row 0: a nonzero in the last column
+    col[rp[rows] - 1] = 0      # last row: a nonzero in the first column
+    d = DevMatrix(codes, lut, bits, rp, col, val, x)
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, bits, rp, col, val, x)
+    yd_ref, sd = oracle.dense_sparse_gemv(codes, lut, bits, None, None, None, x)
+    step(f"maximum columns bits={bits} batch={batch} nnz={col.size}")
+    y_fused = d.fused()
+    y_dense = d.gemv()
+    y_pair = d.gemv()
+    d.spmv_add(y_pair)
+    y_group = torch.full((batch, rows), float("nan"), dtype=torch.float16, device="cuda")
+    nw().dense_sparse_gemv_group(_items([d], [y_group]), bits)
+    y_noalloc = torch.full((batch, rows), float("nan"), dtype=torch.float16, device="cuda")
+    nw().dense_sparse_gemv_noalloc(d.packed, d.lut, bits, d.row_ptr, d.col, d.val, d.x, y_noalloc)
+    torch.cuda.synchronize()
+    assert_close(y_fused, y_ref, scale, TOL, "fused")
+    assert_close(y_dense, yd_ref, sd, TOL, "dense only")
+    assert_close(y_pair, y_ref, scale, TOL, "stream-ordered")
+    assert_close(y_group, y_ref, scale, TOL, "group")
+    assert np.array_equal(dev_to_u16(y_noalloc), dev_to_u16(y_fused)), "allocation-free call differs from the fused call"
