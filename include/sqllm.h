@@ -397,8 +397,11 @@ sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves
  *   groups per workgroup, waves per workgroup of its launch, 1 if its
  *   outliers read a transposed copy of x, and for a single call run as two
  *   row slices the row tiles of the first slice (which runs at the split
- *   given; the rest runs whole), else 0; plan[5 n] = 1 for the matrix-core
- *   form.  Argument and workspace errors as the calls report them. */
+ *   given; the rest runs whole), else 0; plan[5 n]: bit 0 set for the
+ *   matrix-core form, bit 1 set when the outlier launch takes the compact
+ *   3-bit pair table (64 pair entries per lane instead of 256, which leaves
+ *   room in LDS for x).  Argument and workspace errors as the calls report
+ *   them. */
 sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const int64_t *cols, const int64_t *nnz,
                                     int batch, size_t workspace_bytes, int *plan);
 sqllm_status sqllm_test_decode(const void *packed, const uint16_t *lut, int64_t rows, int64_t cols, int bits,

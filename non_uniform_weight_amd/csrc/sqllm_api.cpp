@@ -180,26 +180,39 @@ int use_mf(int batch) { return tuning().dot_only && batch <= kMaxDotBatch ? 0 : 
 
 // Stage x in LDS for the outlier gathers when it fits beside the pair table
 // (in half of the LDS when the launch has more workgroups than units, so
-// that two share a unit).
-void choose_x_lds(KernelArgs &a, int batch, int64_t nnz, int64_t workgroups, LaunchShape &ls)
+// that two share a unit).  The compact 3-bit table is taken (for the whole
+// launch) only when some product's x fits beside it and not beside the full
+// table; a launch of products that all fit, or none, keeps the full table.
+// a[0..n): the launch's products (all fused when nnz > 0).
+void choose_x_lds(KernelArgs *a, int n, int bits, int batch, int64_t nnz, int64_t workgroups, LaunchShape &ls)
 {
-    a.x_lds = 0;
-    if (nnz <= 0) return;
-    const size_t staged = staged_x_bytes(a.cols, batch);
     const size_t budget = workgroups > tuning().target_wgs ? kLdsBudget / 2 : kLdsBudget;
-    if (kTableBytes + staged <= budget) {
-        a.x_lds = 1;
-        if (staged > ls.dyn_lds) ls.dyn_lds = staged;
+    const size_t full = static_lds_bytes(true, batch, false), compact = static_lds_bytes(true, batch, true);
+    ls.compact = 0;
+    for (int k = 0; k < n; ++k) {
+        a[k].x_lds = 0;
+        const size_t staged = staged_x_bytes(a[k].cols, batch);
+        if (nnz > 0 && ls.mf && compact_allowed(bits, batch) && full + staged > budget && compact + staged <= budget)
+            ls.compact = 1;
+    }
+    if (nnz <= 0) return;
+    const size_t table = ls.compact ? compact : full;
+    for (int k = 0; k < n; ++k) {
+        const size_t staged = staged_x_bytes(a[k].cols, batch);
+        if (table + staged <= budget) {
+            a[k].x_lds = 1;
+            if (staged > ls.dyn_lds) ls.dyn_lds = staged;
+        }
     }
 }
 
-void choose_dense(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
+void choose_dense(KernelArgs &a, int bits, int batch, int64_t nnz, LaunchShape &ls)
 {
     choose_split(a, a.tiles);
     ls.mf = use_mf(batch);
     ls.waves = choose_waves((int64_t)a.tiles * a.split, a.gps);
     ls.dyn_lds = 0;
-    choose_x_lds(a, batch, nnz, (int64_t)a.tiles * a.split, ls);
+    choose_x_lds(&a, 1, bits, batch, nnz, (int64_t)a.tiles * a.split, ls);
 }
 
 // Outlier-only kernel: about kSparseShare nonzeros per wave; x staged in LDS
@@ -218,7 +231,7 @@ void choose_sparse(KernelArgs &a, int batch, int64_t nnz, LaunchShape &ls)
     a.gps = 0;
     ls.waves = waves;
     const size_t staged = staged_x_bytes(a.cols, batch);
-    a.x_lds = static_lds_bytes(false, batch) + staged <= (size_t)kLdsBudget;
+    a.x_lds = static_lds_bytes(false, batch, false) + staged <= (size_t)kLdsBudget;
     ls.dyn_lds = a.x_lds ? staged : 0;
 }
 
@@ -296,7 +309,7 @@ KernelArgs base_args(int64_t rows, int64_t cols, const uint16_t *x, uint16_t *y,
 sqllm_status plan_single(KernelArgs &a, int bits, int batch, int64_t nnz, void *ws, size_t ws_bytes, LaunchShape &ls,
                          XtJobs &jobs, GroupArgs &g, bool &sliced)
 {
-    choose_dense(a, batch, nnz, ls);
+    choose_dense(a, bits, batch, nnz, ls);
     sqllm_status st = workspace_checks(a.split, a.rows, batch, ws, ws_bytes);
     if (st != SQLLM_OK) return st;
     plan_xt(a, batch, nnz, nnz, ws, ws_bytes, jobs);
@@ -308,7 +321,7 @@ sqllm_status plan_single(KernelArgs &a, int bits, int batch, int64_t nnz, void *
 // One launch of a group call: the products with outliers (fused) or those
 // without.  g.n = 0 when there are none; which[k] is the item index of
 // g.item[k].
-sqllm_status plan_group_pass(const sqllm_product *items, int n, int batch, bool fused, void *workspace,
+sqllm_status plan_group_pass(const sqllm_product *items, int n, int bits, int batch, bool fused, void *workspace,
                              size_t workspace_bytes, GroupArgs &g, LaunchShape &ls, XtJobs &jobs, int *which)
 {
     g = GroupArgs{};
@@ -371,7 +384,7 @@ sqllm_status plan_group_pass(const sqllm_product *items, int n, int batch, bool 
         if (g.item[k].gps > max_gps) max_gps = g.item[k].gps;
     ls.waves = choose_waves(wgs, max_gps);
     // products that share x (as q, k and v do) share one transposed copy
-    for (int k = 0; k < g.n; ++k) choose_x_lds(g.item[k], batch, fused ? 1 : 0, wgs, ls);
+    choose_x_lds(g.item, g.n, bits, batch, fused ? 1 : 0, wgs, ls);
     for (int k = 0; k < g.n; ++k) {
         int64_t nnz_x = 0; // nonzeros of this launch's products that gather from the same x
         for (int j = 0; j < g.n; ++j)
@@ -589,7 +602,7 @@ sqllm_status sqllm_dense_sparse_gemv_group(const sqllm_product *items, int n, in
         LaunchShape ls;
         XtJobs jobs;
         int which[kMaxGroup];
-        sqllm_status st = plan_group_pass(items, n, batch, fused, workspace, workspace_bytes, g, ls, jobs, which);
+        sqllm_status st = plan_group_pass(items, n, bits, batch, fused, workspace, workspace_bytes, g, ls, jobs, which);
         if (st != SQLLM_OK) return st;
         if (g.n == 0) continue;
         // one product: the single-product kernel (its arguments come without
@@ -777,7 +790,7 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
         plan[2] = ls.waves;
         plan[3] = a.xt ? 1 : 0;
         plan[4] = sliced ? g.item[0].tiles : 0;
-        plan[5] = ls.mf;
+        plan[5] = ls.mf | (ls.compact << 1);
         return SQLLM_OK;
     }
     sqllm_product items[kMaxGroup] = {}; // no outlier plans
@@ -794,13 +807,13 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
         p.x = (const uint16_t *)fake(mode == 2 ? 0 : i, 0);
         p.y = (uint16_t *)fake(i, 1);
     }
-    int mf = use_mf(batch);
+    int mf = use_mf(batch), compact = 0;
     for (int pass = 0; pass < 2; ++pass) {
         GroupArgs g;
         LaunchShape ls;
         XtJobs jobs;
         int which[kMaxGroup];
-        const sqllm_status st = plan_group_pass(items, n, batch, pass == 0, ws, workspace_bytes, g, ls, jobs, which);
+        const sqllm_status st = plan_group_pass(items, n, 3, batch, pass == 0, ws, workspace_bytes, g, ls, jobs, which);
         if (st != SQLLM_OK) return st;
         for (int k = 0; k < g.n; ++k) {
             int *q = plan + 5 * which[k];
@@ -811,8 +824,9 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
             q[4] = 0;
         }
         if (g.n) mf = ls.mf;
+        if (g.n && ls.compact) compact = 1;
     }
-    plan[5 * n] = mf;
+    plan[5 * n] = mf | (compact << 1);
     return SQLLM_OK;
 }
 

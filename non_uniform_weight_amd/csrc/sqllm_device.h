@@ -109,8 +109,10 @@ __device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32
     return r;
 }
 
-// Pair-table byte address of pair P (0..127) of a group held in d[].
-template <int BITS, int P>
+// Pair-table byte address of pair P (0..127) of a group held in d[].  CT:
+// the compact 3-bit table, which takes the address bytes with their top two
+// bits cleared.
+template <int BITS, int P, bool CT>
 __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lane4)
 {
     if constexpr (BITS == 4) {
@@ -127,8 +129,9 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
             return __builtin_amdgcn_perm(d[P >> 3] >> 4, lane4, addr_sel<k>());
     } else {
         constexpr int u = P / 16, pu = P % 16;
+        constexpr uint32_t keep = CT ? 0x3F3F3F3Fu : 0xFFFFFFFFu;
         if constexpr (pu < 12) {
-            return __builtin_amdgcn_perm(d[3 * u + pu / 4], lane4, addr_sel<pu % 4>());
+            return __builtin_amdgcn_perm(d[3 * u + pu / 4] & keep, lane4, addr_sel<pu % 4>());
         } else {
             // pair 12+q of the unit: bits [2k, 2k+2) are the top bits of unit
             // byte 4k+q.  Byte q of `top` gets them at bits 2k..2k+1 by two
@@ -136,7 +139,7 @@ __device__ __forceinline__ uint32_t pair_address(const uint32_t *d, uint32_t lan
             // copies over the top two index bits ignore.
             const uint32_t t01 = bit_insert(0x03030303u, d[3 * u] >> 6, d[3 * u + 1] >> 4);
             const uint32_t top = bit_insert(0x0F0F0F0Fu, t01, d[3 * u + 2] >> 2);
-            return __builtin_amdgcn_perm(top, lane4, addr_sel<pu - 12>());
+            return __builtin_amdgcn_perm(top & keep, lane4, addr_sel<pu - 12>());
         }
     }
 }
@@ -224,13 +227,13 @@ constexpr int acc_chains(int batch) { return batch == 1 ? 3 : (batch == 2 ? 2 : 
 // (instead of one per read) covers them.
 constexpr int kBatch = 8;
 
-template <int BITS, int B, bool MF, int Q>
+template <int BITS, int B, bool MF, int Q, bool CT>
 __device__ __forceinline__ void batch_reads(const GroupRegs<BITS, B, MF> &r, uint32_t lane4, const uint32_t *tab,
                                             uint32_t (&wv)[kBatch])
 {
     uint32_t addr[kBatch];
     [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
-        ((addr[Ks] = pair_address<BITS, Q * kBatch + Ks>(r.d, lane4)), ...);
+        ((addr[Ks] = pair_address<BITS, Q * kBatch + Ks, CT>(r.d, lane4)), ...);
     }(std::make_integer_sequence<int, kBatch>{});
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) wv[k] = *(const uint32_t *)((const char *)tab + addr[k]);
@@ -397,17 +400,17 @@ __device__ __forceinline__ void batch_macs(const GroupRegs<BITS, B, false> &r, c
 }
 
 // All 128 pairs (256 codes) of one group.
-template <int BITS, int B>
+template <int BITS, int B, bool CT>
 __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, false> &r, uint32_t lane4, const uint32_t *tab,
                                           float *acc)
 {
     constexpr int NQ = 128 / kBatch;
     uint32_t wv[2][kBatch];
-    batch_reads<BITS, B, false, 0>(r, lane4, tab, wv[0]);
+    batch_reads<BITS, B, false, 0, CT>(r, lane4, tab, wv[0]);
     [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
         (
             [&] {
-                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, false, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
+                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, false, Qs + 1, CT>(r, lane4, tab, wv[(Qs + 1) & 1]);
                 // one wait for the whole batch: the empty statement needs all
                 // eight table reads of batch Qs
                 const uint32_t(&cur)[kBatch] = wv[Qs & 1];
@@ -452,17 +455,17 @@ __device__ __forceinline__ void mf_step(const GroupRegs<BITS, B, true> &r, const
     }
 }
 
-template <int BITS, int B>
+template <int BITS, int B, bool CT>
 __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, true> &r, uint32_t lane4, const uint32_t *tab,
                                           f32x4 (&macc)[mf_quads(B)][2])
 {
     constexpr int NQ = 128 / kBatch; // 16 batches of 8 pairs (16 columns, 4 steps of 4)
     uint32_t wv[2][kBatch];
-    batch_reads<BITS, B, true, 0>(r, lane4, tab, wv[0]);
+    batch_reads<BITS, B, true, 0, CT>(r, lane4, tab, wv[0]);
     [&]<int... Qs>(std::integer_sequence<int, Qs...>) {
         (
             [&] {
-                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, true, Qs + 1>(r, lane4, tab, wv[(Qs + 1) & 1]);
+                if constexpr (Qs + 1 < NQ) batch_reads<BITS, B, true, Qs + 1, CT>(r, lane4, tab, wv[(Qs + 1) & 1]);
                 const uint32_t(&cw)[kBatch] = wv[Qs & 1];
                 mf_step<BITS, B, 4 * Qs + 0>(r, cw, macc);
                 mf_step<BITS, B, 4 * Qs + 1>(r, cw, macc);
@@ -473,9 +476,10 @@ __device__ __forceinline__ void mac_group(const GroupRegs<BITS, B, true> &r, uin
     }(std::make_integer_sequence<int, NQ>{});
 }
 
-// Pair table of the tile (256 entries per lane).  Work item (lane l, low
-// code h): lo = LUT[row][h]; for every high code c, entry h | c << b (3-bit:
-// also with both ignored top bits set every way) = lo | LUT[row][c] << 16.
+// Pair table of the tile (256 entries per lane; 64 when compact).  Work item
+// (lane l, low code h): lo = LUT[row][h]; for every high code c, entry
+// h | c << b (3-bit, full table: also with both ignored top bits set every
+// way) = lo | LUT[row][c] << 16.
 // A thread's items idx = threadIdx.x + k * blockDim.x (k < N) all belong to
 // lane idx % 64, so they share one load of the row's table.  The loads are
 // issued apart from the stores so that they go out ahead of the code loads.
@@ -513,7 +517,7 @@ __device__ __forceinline__ void table_items_load(TableItems<BITS, N> &it, const 
     }
 }
 
-template <int BITS, int N>
+template <int BITS, int N, bool CT>
 __device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it, uint32_t *tab, int idx0, int stride)
 {
     constexpr int E = Format<BITS>::kEntries;
@@ -531,6 +535,8 @@ __device__ __forceinline__ void table_items_store(const TableItems<BITS, N> &it,
             } else if constexpr (BITS == 2) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) tab[(h | (c << 2) | (j << 4)) * 64 + l] = v;
+            } else if constexpr (CT) {
+                tab[(h | (c << 3)) * 64 + l] = v;
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) tab[(h | (c << 3) | (j << 6)) * 64 + l] = v;
@@ -855,7 +861,7 @@ __device__ __forceinline__ void load_args_now(const KernelArgs &a)
                  "s"(a.x_lds), "s"(a.xt), "s"(a.sparse_naive), "s"(a.plan), "s"(a.helpers), "s"(blockDim.x));
 }
 
-template <int BITS, int B, int MODE, bool MF>
+template <int BITS, int B, int MODE, bool MF, bool CT>
 __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
 {
     load_args_now(a);
@@ -866,7 +872,8 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     constexpr int E = Format<BITS>::kEntries;
     constexpr int D = ring_depth(BITS, B, MF);
     constexpr int ITEMS = DENSE && E >= 8 ? (64 * E) / 512 : 1; // table items per thread with 8 waves
-    __shared__ __align__(16) uint32_t tab[DENSE ? kTableBytes / 4 : kMaxWaves * B * 64];
+    static_assert(!CT || (compact_allowed(BITS, B) && MF && MODE == kFused), "compact table: 3-bit fused, matrix cores");
+    __shared__ __align__(16) uint32_t tab[DENSE ? dense_lds_bytes(B, CT) / 4 : kMaxWaves * B * 64];
     extern __shared__ __align__(16) uint32_t dyn[];
 
     const int nt = blockDim.x;
@@ -914,7 +921,7 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
         for (int idx = threadIdx.x + ITEMS * nt; idx < 64 * E; idx += nt) {
             TableItems<BITS, 1> it2;
             table_items_load<BITS, 1>(it2, a.lut, idx, nt, row0, a.rows);
-            table_items_store<BITS, 1>(it2, tab, idx, nt);
+            table_items_store<BITS, 1, CT>(it2, tab, idx, nt);
         }
     }
 
@@ -953,9 +960,9 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     };
     auto dense_math = [&](const GroupRegs<BITS, B, MF> &r) {
         if constexpr (DENSE && MF)
-            mac_group<BITS, B>(r, lane4, tab, macc);
+            mac_group<BITS, B, CT>(r, lane4, tab, macc);
         else if constexpr (DENSE)
-            mac_group<BITS, B>(r, lane4, tab, acc);
+            mac_group<BITS, B, CT>(r, lane4, tab, acc);
     };
     if constexpr (!kRingAfterTable) issue_ring();
 
@@ -982,13 +989,22 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     // -- 5. store the pair table and the staged x, then a barrier that
     //       orders LDS only: the ring stays in flight across it
     if constexpr (DENSE) {
-        if ((int)threadIdx.x < 64 * E) table_items_store<BITS, ITEMS>(items, tab, threadIdx.x, nt);
+        if ((int)threadIdx.x < 64 * E) table_items_store<BITS, ITEMS, CT>(items, tab, threadIdx.x, nt);
     }
     if constexpr (SPARSE) {
 #pragma unroll
         for (int k = 0; k < kStageQuads; ++k)
             if ((int)threadIdx.x + k * nt < nxq) ((u32x4 *)xstage)[threadIdx.x + k * nt] = xq[k];
-        for (int i = threadIdx.x + kStageQuads * nt; i < nxq; i += nt) ((u32x4 *)xstage)[i] = ((const u32x4 *)a.x)[i];
+        // the rest kStageQuads quads per thread at a time: all of a batch's
+        // loads go out before its stores wait for them
+        for (int i0 = threadIdx.x + kStageQuads * nt; i0 < nxq; i0 += kStageQuads * nt) {
+            u32x4 v[kStageQuads];
+#pragma unroll
+            for (int k = 0; k < kStageQuads; ++k) v[k] = ((const u32x4 *)a.x)[min(i0 + k * nt, nxq - 1)];
+#pragma unroll
+            for (int k = 0; k < kStageQuads; ++k)
+                if (i0 + k * nt < nxq) ((u32x4 *)xstage)[i0 + k * nt] = v[k];
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (kRingAfterTable) issue_ring();
@@ -1124,10 +1140,10 @@ __device__ __forceinline__ void product_body(const KernelArgs &a, int bid)
     finish_rows<B, ADDY>(a, t, s, lane, tot, a.split, count - a.split, a.helpers > 0 ? kMaxSplit - 1 : count - 1);
 }
 
-template <int BITS, int B, int MODE, bool MF>
+template <int BITS, int B, int MODE, bool MF, bool CT>
 __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs a)
 {
-    product_body<BITS, B, MODE, MF>(a, blockIdx.x);
+    product_body<BITS, B, MODE, MF, CT>(a, blockIdx.x);
 }
 
 // Several independent products in one launch: the workgroups of row y of the
@@ -1136,13 +1152,13 @@ __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_kernel(KernelArgs
 // room, so one product's start-up (table rows, first code latency) and tail
 // (reductions) overlap the other products' code streams.  The product index
 // is blockIdx.y, so its arguments come in one round of scalar loads.
-template <int BITS, int B, int MODE, bool MF>
+template <int BITS, int B, int MODE, bool MF, bool CT>
 __global__ void __launch_bounds__(kMaxWaves * 64) dense_sparse_group_kernel(GroupArgs g)
 {
     const KernelArgs &a = g.item[blockIdx.y];
     load_args_now(a);
     if ((int)blockIdx.x >= a.tiles * a.split + a.helpers) return;
-    product_body<BITS, B, MODE, MF>(a, blockIdx.x);
+    product_body<BITS, B, MODE, MF, CT>(a, blockIdx.x);
 }
 
 // Ask once per kernel and device for more than the default dynamic LDS (the
@@ -1163,25 +1179,24 @@ inline void raise_lds_limit(const void *kern, std::atomic<uint64_t> &done, int b
     done.fetch_or(bit, std::memory_order_relaxed);
 }
 
-template <int BITS, int B, int MODE, bool MF>
+template <int BITS, int B, int MODE, bool MF, bool CT>
 hipError_t launch_one(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
-    auto kern = dense_sparse_kernel<BITS, B, MODE, MF>;
+    auto kern = dense_sparse_kernel<BITS, B, MODE, MF, CT>;
     static std::atomic<uint64_t> attr_devices{0};
-    raise_lds_limit((const void *)kern, attr_devices,
-                    kLdsBudget - (MODE != kSparseAdd ? kTableBytes : kMaxWaves * B * 64 * 4));
+    raise_lds_limit((const void *)kern, attr_devices, kLdsBudget - (int)static_lds_bytes(MODE != kSparseAdd, B, CT));
     if (ls.waves < 1 || ls.waves > kMaxWaves) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(a.tiles * a.split + a.helpers)), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, a);
     return hipGetLastError();
 }
 
-template <int BITS, int B, int MODE, bool MF>
+template <int BITS, int B, int MODE, bool MF, bool CT>
 hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
-    auto kern = dense_sparse_group_kernel<BITS, B, MODE, MF>;
+    auto kern = dense_sparse_group_kernel<BITS, B, MODE, MF, CT>;
     static std::atomic<uint64_t> attr_devices{0};
-    raise_lds_limit((const void *)kern, attr_devices, kLdsBudget - kTableBytes);
+    raise_lds_limit((const void *)kern, attr_devices, kLdsBudget - (int)static_lds_bytes(true, B, CT));
     if (ls.waves < 1 || ls.waves > kMaxWaves || g.n < 1 || g.n > kMaxGroup) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)g.wgs, (unsigned)g.n), block((unsigned)(64 * ls.waves));
     hipLaunchKernelGGL(kern, grid, block, ls.dyn_lds, stream, g);
@@ -1190,45 +1205,57 @@ hipError_t launch_group_one(const GroupArgs &g, const LaunchShape &ls, hipStream
 
 // The dense modes in the matrix-core form when the shape asks for it (and
 // always above kMaxDotBatch, where the dot form is not built); the dot form
-// and the outlier-only mode otherwise.
-template <int BITS, int B, int MODE>
+// and the outlier-only mode otherwise.  CT: the compact-table kernels (the
+// fused matrix-core form only).
+template <int BITS, int B, int MODE, bool CT>
 hipError_t launch_group_form(const GroupArgs &g, const LaunchShape &ls, hipStream_t stream)
 {
-    if constexpr (MODE != kSparseAdd)
-        if (ls.mf || B > kMaxDotBatch) return launch_group_one<BITS, B, MODE, true>(g, ls, stream);
-    if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch) return launch_group_one<BITS, B, MODE, false>(g, ls, stream);
-    return hipErrorInvalidValue;
+    if constexpr (CT) {
+        if constexpr (compact_allowed(BITS, B) && MODE == kFused) return launch_group_one<BITS, B, MODE, true, true>(g, ls, stream);
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (MODE != kSparseAdd)
+            if (ls.mf || B > kMaxDotBatch) return launch_group_one<BITS, B, MODE, true, false>(g, ls, stream);
+        if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch)
+            return launch_group_one<BITS, B, MODE, false, false>(g, ls, stream);
+        return hipErrorInvalidValue;
+    }
 }
 
-template <int BITS, int B, int MODE>
+template <int BITS, int B, int MODE, bool CT>
 hipError_t launch_form(const KernelArgs &a, const LaunchShape &ls, hipStream_t stream)
 {
-    if constexpr (MODE != kSparseAdd)
-        if (ls.mf || B > kMaxDotBatch) return launch_one<BITS, B, MODE, true>(a, ls, stream);
-    if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch) return launch_one<BITS, B, MODE, false>(a, ls, stream);
-    return hipErrorInvalidValue;
+    if constexpr (CT) {
+        if constexpr (compact_allowed(BITS, B) && MODE == kFused) return launch_one<BITS, B, MODE, true, true>(a, ls, stream);
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (MODE != kSparseAdd)
+            if (ls.mf || B > kMaxDotBatch) return launch_one<BITS, B, MODE, true, false>(a, ls, stream);
+        if constexpr (MODE == kSparseAdd || B <= kMaxDotBatch) return launch_one<BITS, B, MODE, false, false>(a, ls, stream);
+        return hipErrorInvalidValue;
+    }
 }
 
-// Batches LO..HI of one (bits, mode).  The batch-1..8 kernels and the
-// batch-9..16 ones are instantiated in separate translation units: sharing
-// one unit changes the compiler's code for the small batches (measured 6%
-// slower at batch 1).
-template <int BITS, int MODE, int LO, int HI>
+// Batches LO..HI of one (bits, mode).  The batch-1..8 kernels, the
+// batch-9..16 ones and the compact-table ones are instantiated in separate
+// translation units: sharing one unit changes the compiler's code for the
+// small batches (measured 6% slower at batch 1).
+template <int BITS, int MODE, int LO, int HI, bool CT = false>
 hipError_t launch_group_batch(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream)
 {
     hipError_t r = hipErrorInvalidValue;
     [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
-        ((batch == LO + Ks ? (void)(r = launch_group_form<BITS, LO + Ks, MODE>(g, ls, stream)) : void()), ...);
+        ((batch == LO + Ks ? (void)(r = launch_group_form<BITS, LO + Ks, MODE, CT>(g, ls, stream)) : void()), ...);
     }(std::make_integer_sequence<int, HI - LO + 1>{});
     return r;
 }
 
-template <int BITS, int MODE, int LO, int HI>
+template <int BITS, int MODE, int LO, int HI, bool CT = false>
 hipError_t launch_batch(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream)
 {
     hipError_t r = hipErrorInvalidValue;
     [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
-        ((batch == LO + Ks ? (void)(r = launch_form<BITS, LO + Ks, MODE>(a, ls, stream)) : void()), ...);
+        ((batch == LO + Ks ? (void)(r = launch_form<BITS, LO + Ks, MODE, CT>(a, ls, stream)) : void()), ...);
     }(std::make_integer_sequence<int, HI - LO + 1>{});
     return r;
 }

@@ -17,6 +17,21 @@ constexpr int kMaxWaves = 16;     // waves per workgroup
 constexpr int kMaxSplit = 16;     // workgroups sharing one row tile (the owners and any helpers)
 constexpr int kMaxHelpers = 8;    // helpers one row tile may get from an outlier plan
 constexpr int kTableBytes = 256 * 64 * 4;           // pair table: 256 entries x 64 lanes x half2
+// The compact 3-bit pair table: the two top bits of a pair's address byte
+// are masked (one AND per dword of codes), so the table holds the 64 pairs
+// once (16 KB) instead of four times.  A fused launch at batch 2..8 takes it
+// when that is what lets x be staged in LDS for the outlier gathers (x of
+// 22016x8192 at batch 4 beside two tables per compute unit, of 8192x8192 at
+// batch 8 beside one); otherwise the AND costs more than it saves.
+constexpr bool compact_allowed(int bits, int batch) { return bits == 3 && batch >= 2 && batch <= kMaxDotBatch; }
+constexpr int table_bytes(bool compact) { return compact ? 64 * 64 * 4 : kTableBytes; }
+// Static LDS of a dense-mode workgroup: the pair table, which the wave
+// reduction (up to kMaxWaves x batch x 64 floats) reuses once the dense part
+// is done, so at least that.
+constexpr int dense_lds_bytes(int batch, bool compact)
+{
+    return table_bytes(compact) > kMaxWaves * batch * 64 * 4 ? table_bytes(compact) : kMaxWaves * batch * 64 * 4;
+}
 constexpr int kLdsBudget = 160 * 1024;              // LDS per compute unit on gfx950
 constexpr int kSparseShare = 512; // outlier nonzeros per wave the outlier-only kernel aims for
 constexpr int kDefaultWaves = 8;  // waves per workgroup: two workgroups share a compute unit
@@ -59,6 +74,7 @@ struct LaunchShape {
     int waves;                // waves per workgroup
     size_t dyn_lds;           // dynamic LDS bytes (staged x)
     int mf;                   // 1: dense part on the matrix cores, 0: dot form (batch <= kMaxDotBatch)
+    int compact;              // 1: the compact 3-bit pair table (fused, matrix cores, batch 2..8)
 };
 
 hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mode, const LaunchShape &ls,
@@ -122,7 +138,10 @@ hipError_t launch_xt_clear(const XtJobs &j, int batch, hipStream_t stream);
 
 // Static LDS of a kernel: the pair table (dense modes) or the wave
 // reduction area (outlier-only mode).
-inline size_t static_lds_bytes(bool dense, int batch) { return dense ? kTableBytes : (size_t)kMaxWaves * batch * 64 * 4; }
+inline size_t static_lds_bytes(bool dense, int batch, bool compact)
+{
+    return dense ? (size_t)dense_lds_bytes(batch, compact) : (size_t)kMaxWaves * batch * 64 * 4;
+}
 
 } // namespace sqllm
 

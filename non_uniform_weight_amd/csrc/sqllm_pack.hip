@@ -28,6 +28,8 @@ hipError_t launch_group_fused3(const GroupArgs &g, int batch, const LaunchShape 
 hipError_t launch_group_fused4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_group_gemv3(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 hipError_t launch_group_gemv4(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_fused3_compact(const KernelArgs &a, int batch, const LaunchShape &ls, hipStream_t stream);
+hipError_t launch_group_fused3_compact(const GroupArgs &g, int batch, const LaunchShape &ls, hipStream_t stream);
 #define SQLLM_WIDE(bits)                                                                                              \
     hipError_t launch_fused##bits##_wide(const KernelArgs &, int, const LaunchShape &, hipStream_t);                  \
     hipError_t launch_gemv##bits##_wide(const KernelArgs &, int, const LaunchShape &, hipStream_t);                   \
@@ -45,6 +47,7 @@ hipError_t launch_dense_sparse(const KernelArgs &a, int bits, int batch, Mode mo
     const bool wide = batch > kMaxDotBatch;
     switch (mode) {
     case kFused:
+        if (ls.compact) return compact_allowed(bits, batch) ? launch_fused3_compact(a, batch, ls, stream) : hipErrorInvalidValue;
         if (wide)
             return bits == 2   ? launch_fused2_wide(a, batch, ls, stream)
                    : bits == 3 ? launch_fused3_wide(a, batch, ls, stream)
@@ -69,6 +72,7 @@ hipError_t launch_dense_sparse_group(const GroupArgs &g, int bits, int batch, Mo
     const bool wide = batch > kMaxDotBatch;
     switch (mode) {
     case kFused:
+        if (ls.compact) return compact_allowed(bits, batch) ? launch_group_fused3_compact(g, batch, ls, stream) : hipErrorInvalidValue;
         if (wide)
             return bits == 2   ? launch_group_fused2_wide(g, batch, ls, stream)
                    : bits == 3 ? launch_group_fused3_wide(g, batch, ls, stream)

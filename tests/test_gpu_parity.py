@@ -789,6 +789,65 @@ def test_row_slices_for_two_slots(bits, batch, sparsity):
         assert_close(yd[:, sel_dev], yd_ref, dscale, TOL, "sliced dense-only")
 
 
+# ------------------------------------------------------------ the compact 3-bit pair table
+
+# (rows, cols, batch, sparsity): x fits in LDS beside the compact table but not
+# beside the full one -- one workgroup per compute unit at batch 8, 4 and 2,
+# and 301 row tiles (two row slices, two workgroups per unit) at batch 4
+COMPACT_CASES = [(300, 8192, 8, "5pct"), (200, 16384, 4, "dense_row"), (130, 32768, 2, "5pct"),
+                 (64 * 300 + 17, 4096, 4, "empty_rows")]
+
+
+@pytest.mark.parametrize("rows,cols,batch,sparsity", COMPACT_CASES)
+def test_compact_table_launches(rows, cols, batch, sparsity):
+    """Fused 3-bit launches that stage x beside the compact pair table (the
+    64 pair entries once, addressed with the top two bits of each address byte
+    cleared): every row within tolerance of the oracle, repeated calls give
+    the same bits, and integer inputs give exactly the fp16 rounding of the
+    oracle's result."""
+    (plan,), _ = nw().launch_plan([(rows, cols, 1)], batch=batch)
+    assert plan["compact"] == 1 and plan["xt"] == 0
+    rng = np.random.default_rng(stable_seed("compact", rows, cols, batch, sparsity))
+    codes, lut, x, rp, col, val = _make_case(rng, rows, cols, 3, batch, sparsity)
+    d = DevMatrix(codes, lut, 3, rp, col, val, x)
+    step(f"compact table rows={rows} cols={cols} batch={batch} {sparsity}")
+    y1 = d.fused()
+    y2 = d.fused()
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_u16(y1), dev_to_u16(y2)), "repeated calls differ"
+    y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+    assert_close(y1, y_ref, scale, TOL, f"compact {rows}x{cols} batch {batch}")
+    step(f"compact table, integer inputs rows={rows} cols={cols} batch={batch}")
+    codes, lut, x, rp, col, val = _integer_case(rng, rows, cols, 3, batch)
+    d = DevMatrix(codes, lut, 3, rp, col, val, x)
+    y = d.fused()
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+    assert np.array_equal(dev_to_u16(y), oracle.f64_array_to_f16(y_ref))
+
+
+def test_compact_table_group():
+    """A group launch takes the compact table for all its products when one
+    of them needs it to stage x; a product whose x would fit either way, and
+    one without outliers (its own launch, full table), still match."""
+    rng = np.random.default_rng(stable_seed("compact-group"))
+    batch = 8
+    shapes = [(300, 8192, "5pct"), (129, 2048, "dense_row"), (64, 4096, "none")]
+    plans, _ = nw().launch_plan([(r, c, 0 if sp == "none" else 1) for r, c, sp in shapes], batch=batch, mode=1)
+    assert all(p["compact"] == 1 for p in plans)
+    cases = [_make_case(rng, r, c, 3, batch, sp) for r, c, sp in shapes]
+    cases = [(co, lu, xx, None, None, None) if sp == "none" else (co, lu, xx, rp, cl, va)
+             for (co, lu, xx, rp, cl, va), (_, _, sp) in zip(cases, shapes)]
+    mats = [DevMatrix(*case[:2], 3, *case[3:], case[2]) for case in cases]
+    ys = [torch.full((batch, d.rows), float("nan"), dtype=torch.float16, device="cuda") for d in mats]
+    step(f"compact group batch {batch}: {shapes}")
+    nw().dense_sparse_gemv_group(_items(mats, ys), 3)
+    torch.cuda.synchronize()
+    for (codes, lut, x, rp, col, val), y, shape in zip(cases, ys, shapes):
+        y_ref, scale = oracle.dense_sparse_gemv(codes, lut, 3, rp, col, val, x)
+        assert_close(y, y_ref, scale, TOL, f"compact group item {shape}")
+
+
 @pytest.mark.parametrize("batch", [4, 6, 8])
 def test_group_shared_x(batch):
     """Products that share one x (as q, k and v do) share one transposed copy
