@@ -394,8 +394,9 @@ sqllm_status sqllm_test_tuning(int target_wgs, int min_gps, int split, int waves
  *   products (equal cols).  rows / cols / nnz: HOST arrays of n; workspace_bytes
  *   as the call would get it (0: no workspace).  plan: HOST array of 5 n + 1
  *   ints; for product i, plan[5 i ..] = split (workgroups per row tile), column
- *   groups per workgroup, waves per workgroup of its launch, 1 if its
- *   outliers read a transposed copy of x, and for a single call run as two
+ *   groups per workgroup, waves per workgroup of its launch, where its
+ *   outliers read x (0 in place, 1 a transposed copy, 2 staged in LDS), and
+ *   for a single call run as two
  *   row slices the row tiles of the first slice (which runs at the split
  *   given; the rest runs whole), else 0; plan[5 n]: bit 0 set for the
  *   matrix-core form, bit 1 set when the outlier launch takes the compact

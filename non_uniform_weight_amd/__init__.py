@@ -406,15 +406,17 @@ def set_tuning(target_wgs: int = 0, min_gps: int = 0, split: int = 0, waves: int
 def launch_plan(shapes, batch: int = 1, workspace_bytes: int = 1 << 30, mode: int = 0):
     """Test-only: the launch the calls would make for products of (rows, cols, nnz) in `shapes`, without a
     device.  mode 0: one sqllm_dense_sparse_gemv; 1: one group call, a separate x per product; 2: one
-    group call, one shared x.  Per product: dict(split, gps, waves, xt, slice_tiles, compact); plus the form.
-    compact: the launch takes the compact 3-bit pair table (which leaves room in LDS for x)."""
+    group call, one shared x.  Per product: dict(split, gps, waves, xt, x_lds, slice_tiles, compact); plus the
+    form.  xt: the outliers read a transposed copy of x; x_lds: they read x staged in LDS; compact: the launch
+    takes the compact 3-bit pair table (which leaves room in LDS for x)."""
     n = len(shapes)
     arr = lambda k: (_i64 * n)(*[int(sh[k]) for sh in shapes])
     out = (_i32 * (5 * n + 1))()
     _check(_lib.sqllm_test_launch_plan(mode, n, arr(0), arr(1), arr(2), batch, workspace_bytes, out),
            "sqllm_test_launch_plan")
-    items = [dict(split=out[5 * i], gps=out[5 * i + 1], waves=out[5 * i + 2], xt=out[5 * i + 3],
-                  slice_tiles=out[5 * i + 4], compact=int(bool(out[5 * n] & 2))) for i in range(n)]
+    items = [dict(split=out[5 * i], gps=out[5 * i + 1], waves=out[5 * i + 2], xt=int(out[5 * i + 3] == 1),
+                  x_lds=int(out[5 * i + 3] == 2), slice_tiles=out[5 * i + 4], compact=int(bool(out[5 * n] & 2)))
+             for i in range(n)]
     return items, ("matrix" if out[5 * n] & 1 else "dot")
 
 

@@ -788,7 +788,7 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
         plan[0] = sliced ? g.item[0].split : a.split;
         plan[1] = sliced ? g.item[0].gps : a.gps;
         plan[2] = ls.waves;
-        plan[3] = a.xt ? 1 : 0;
+        plan[3] = a.xt ? 1 : (a.x_lds ? 2 : 0);
         plan[4] = sliced ? g.item[0].tiles : 0;
         plan[5] = ls.mf | (ls.compact << 1);
         return SQLLM_OK;
@@ -820,7 +820,7 @@ sqllm_status sqllm_test_launch_plan(int mode, int n, const int64_t *rows, const 
             q[0] = g.item[k].split;
             q[1] = g.item[k].gps;
             q[2] = ls.waves;
-            q[3] = g.item[k].xt ? 1 : 0;
+            q[3] = g.item[k].xt ? 1 : (g.item[k].x_lds ? 2 : 0);
             q[4] = 0;
         }
         if (g.n) mf = ls.mf;

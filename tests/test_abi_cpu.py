@@ -444,13 +444,14 @@ def test_compact_table_rule(nwpkg):
     def compact(shapes, batch, mode=0):
         return [p["compact"] for p in nwpkg.launch_plan(shapes, batch=batch, mode=mode)[0]]
     assert compact([P65[0]], 8) == [1]            # 128 KB of x: beside 32 KB, not beside 64 KB
-    assert nwpkg.launch_plan([P65[0]], batch=8)[0][0]["xt"] == 0
+    assert [nwpkg.launch_plan([P65[0]], batch=8)[0][0][k] for k in ("xt", "x_lds")] == [0, 1]
     assert compact([P65[0]], 1) == [0]            # batch 1: the full table only
     assert compact([P65[1]], 4) == [1]            # two workgroups per unit: 64 KB of x beside 16 KB
     assert compact([P65[1]], 8) == [0]            # fits neither way: the transposed x
-    assert nwpkg.launch_plan([P65[1]], batch=8)[0][0]["xt"] == 1
+    assert [nwpkg.launch_plan([P65[1]], batch=8)[0][0][k] for k in ("xt", "x_lds")] == [1, 0]
     assert compact([P65[2]], 2) == [0]            # 88 KB of x fits beside the full table
     assert compact([P65[2]], 4) == [0]            # 176 KB fits neither way
+    assert [nwpkg.launch_plan([P65[2]], batch=4)[0][0][k] for k in ("xt", "x_lds")] == [0, 0]  # read in place
     assert compact([(8192, 8192, 0)], 8) == [0]   # no outliers, no staged x
     assert compact([P65[0]] * 3, 4, mode=2) == [1, 1, 1]
     assert compact([(2048, 6144, 9000)], 9) == [0]  # above batch 8 the full table, though x would fit beside a compact one
