@@ -522,19 +522,21 @@ def single_matrix_timing(spec, wl: int, index: int, seed: int, stream, calls_per
 
 
 def per_matrix(seed: int, stream) -> dict:
-    """The single-matrix workloads at batch 1, cold (copies >= 1 GB), one
-    fused call per product in a HIP graph: LLaMA-7B q_proj 4096x4096 3-bit,
-    the 7B MLP pair up 11008x4096 + down 4096x11008 4-bit, the LLaMA-13B
-    layer's seven linears 3-bit with Zipf rows, and the LLaMA-65B shapes
-    8192x8192, 22016x8192, 8192x22016 3-bit; all with 0.45% outliers."""
+    """The single-matrix workloads, cold (copies >= 1 GB), one fused call per
+    product in a HIP graph: LLaMA-7B q_proj 4096x4096 3-bit, the 7B MLP pair
+    up 11008x4096 + down 4096x11008 4-bit, the LLaMA-13B layer's seven
+    linears 3-bit with Zipf rows, all at batch 1, and the LLaMA-65B shapes
+    8192x8192, 22016x8192, 8192x22016 3-bit at batch 1, 2, 4 and 8; all with
+    0.45% outliers.  Keys of batches above 1 end in _b<batch>."""
     import synth
 
     names = {1: "llama7b", 2: "llama7b_mlp", 3: "llama13b", 4: "llama65b"}
     out = {}
-    for wl in (1, 2, 3, 4):
-        for i, spec in enumerate(synth.workload(wl, batch=1) if wl == 4 else synth.workload(wl)):
+    runs = [(wl, 1) for wl in (1, 2, 3, 4)] + [(4, b) for b in (2, 4, 8)]
+    for wl, batch in runs:
+        for i, spec in enumerate(synth.workload(wl, batch=batch) if wl == 4 else synth.workload(wl)):
             r = single_matrix_timing(spec, wl, i, seed, stream)
-            key = f"{names[wl]}_{spec.name}_{spec.rows}x{spec.cols}_{spec.bits}bit"
+            key = f"{names[wl]}_{spec.name}_{spec.rows}x{spec.cols}_{spec.bits}bit" + (f"_b{batch}" if batch > 1 else "")
             out[key] = {"us_per_gemv": r["graph_us"], "GB_per_s": r["GB_per_s"],
                         "frac": round(r["GB_per_s"] / HBM_PEAK_GBS, 4), "nnz": r["nnz"], "copies": r["copies"]}
             log(f"per matrix {key}: {r['graph_us']:.2f} us, {r['GB_per_s']:.0f} GB/s")
