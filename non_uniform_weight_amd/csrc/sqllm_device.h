@@ -17,7 +17,8 @@
 //   v_perm_b32 straight from a packed byte (4-bit: every pair is a byte;
 //   3-bit: 12 of 16 pairs are the low six bits of a byte and the table repeats
 //   over the two ignored top bits, the other 4 pairs are gathered from the top
-//   bits).  The products run on the matrix cores (MF, the default): two
+//   bits; the compact 3-bit table instead clears those two bits, one AND per
+//   dword, and holds each pair once, which leaves LDS for a wider x).  The products run on the matrix cores (MF, the default): two
 //   lookups are a row's 4 consecutive weights, the B operand of one
 //   v_mfma_f32_4x4x4f16 step whose A (the same 4 activations of 4 batch
 //   columns for every row) is broadcast from the one block of lanes that
