@@ -31,8 +31,9 @@ def _with_workspace(d: DevMatrix) -> torch.Tensor:
 # splits its 128 row tiles in two and gathers from the transposed x (811K
 # outliers at batch 6); the second, smaller one splits 16 tiles eight ways at
 # batch 1; the third, smaller still, has no outliers and splits 5 tiles four
-# ways.
-CASES = [(8192, 22016, 3, 6, 45), (1024, 16384, 4, 1, 45), (300, 8192, 3, 2, 0)]
+# ways; the fourth stages x (128 KB at batch 8) beside the compact 3-bit pair
+# table.
+CASES = [(8192, 22016, 3, 6, 45), (1024, 16384, 4, 1, 45), (300, 8192, 3, 2, 0), (300, 8192, 3, 8, 45)]
 
 
 def test_noalloc_equals_workspace_call_on_consecutive_calls():
@@ -42,6 +43,7 @@ def test_noalloc_equals_workspace_call_on_consecutive_calls():
         mats.append((spec, synth.make_matrix(spec, seed=0, workload=9, index=i)))
     plans = [nw().launch_plan([(s.rows, s.cols, s.nnz)], batch=s.batch)[0][0] for s, _ in mats]
     assert plans[0]["split"] == 2 and plans[0]["xt"] == 1 and plans[1]["split"] == 8 and plans[2]["split"] == 4
+    assert plans[3]["compact"] == 1 and plans[3]["x_lds"] == 1
     for (spec, m), plan in zip(mats, plans):
         step(f"noalloc {spec.rows}x{spec.cols} bits {spec.bits} batch {spec.batch} nnz {spec.nnz} plan {plan}")
         d = DevMatrix.from_synth(m)
